@@ -1,0 +1,228 @@
+"""Attention by definition, in float64, materialising S and P.
+
+Test infrastructure only (see the package docstring for who may import it).
+
+Definitions followed
+--------------------
+* [HUB] section "How it works": S = Q K^T / sqrt(d), P = softmax(S), O = P V,
+  computed as three separate steps; the per-row logsumexp L_i = m_i + log l_i
+  is what the fused kernel saves, and the backward pass recomputes
+  P_ij = exp(S_ij - L_i) from it.
+* [LIB] section "The trick that made it all possible: online softmax": the
+  safe softmax (row maximum m subtracted before exponentiating) and the online
+  recurrence m' = max(m, m_new), l' = exp(m - m') l + sum exp(x - m'), with
+  the partial output rescaled by the same factor; dividing by the final l is
+  exact.
+* [LIB] section "Cases where FlashAttention does not help": the causal mask
+  is one of the masks the kernels ship.
+
+Readings where the pages are silent
+-----------------------------------
+* The scale is an argument; the oracle uses float64(float32(scale)) so that it
+  is bit-identical to the float32 scale the kernels receive.
+* Causal: query i sees key j iff j <= i (lower triangle, diagonal included,
+  N_q == N_k), so no row is ever fully masked.
+* LSE uses the natural logarithm of the sum over the *scaled* scores.
+* Backward: the pages only say that P is recomputed from L. The gradients
+  below are the derivative of the forward definition (chain rule through the
+  softmax): dV = P^T dO, dP = dO V^T, D_i = sum_j P_ij dP_ij,
+  dS = P * (dP - D), dQ = s dS K, dK = s dS^T Q.
+
+Arrays are ``[B, H, N, d]`` (row-major, d fastest); LSE and D are ``[B, H, N]``.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+def scale_as_f32(scale: float) -> float:
+    """The float32 value of ``scale``, widened exactly to float64."""
+    return float(np.float32(scale))
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d) ([HUB] "How it works")."""
+    return 1.0 / math.sqrt(d)
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def head_scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
+                rows: np.ndarray | None = None) -> np.ndarray:
+    """S = s Q K^T for one head, with masked entries set to -inf.
+
+    ``rows`` selects query rows (absolute indices) so that large heads can be
+    evaluated a few rows at a time; each row of S depends only on its own query.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    idx = np.arange(q.shape[0]) if rows is None else np.asarray(rows)
+    s = scale_as_f32(scale) * (q[idx] @ k.T)
+    if causal:
+        keys = np.arange(k.shape[0])
+        s[keys[None, :] > idx[:, None]] = -np.inf
+    return s
+
+
+def safe_softmax_rows(s: np.ndarray):
+    """Row-wise safe softmax: returns (P, m, l) with m the row max and l the
+    row sum of exp(S - m) ([LIB] "online softmax", the standard softmax)."""
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    return e / l[:, None], m, l
+
+
+def forward_head(q, k, v, causal: bool, scale: float, rows=None):
+    """O and LSE for one head (or for the query rows in ``rows``)."""
+    s = head_scores(q, k, scale, causal, rows)
+    p, m, l = safe_softmax_rows(s)
+    o = p @ _f64(v)
+    lse = m + np.log(l)
+    return o, lse
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None):
+    """Forward for ``[B, H, N, d]`` inputs: returns (O, LSE) in float64."""
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    o = np.empty((B, H, N, v.shape[-1]))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], causal, scale)
+    return o, lse
+
+
+def probabilities(q, k, causal: bool = False, scale: float | None = None):
+    """P = softmax(S) for one head (exposed for the row-sum invariant)."""
+    if scale is None:
+        scale = default_scale(np.shape(q)[-1])
+    p, _, _ = safe_softmax_rows(head_scores(q, k, scale, causal))
+    return p
+
+
+def backward_head(q, k, v, do, causal: bool, scale: float):
+    """(dQ, dK, dV) for one head by the chain rule through the definition."""
+    q, k, v, do = (_f64(x) for x in (q, k, v, do))
+    s = scale_as_f32(scale)
+    p, _, _ = safe_softmax_rows(head_scores(q, k, scale, causal))
+    dv = p.T @ do
+    dp = do @ v.T
+    dd = (p * dp).sum(axis=1)
+    ds = p * (dp - dd[:, None])
+    dq = s * (ds @ k)
+    dk = s * (ds.T @ q)
+    return dq, dk, dv
+
+
+def backward(q, k, v, do, causal: bool = False, scale: float | None = None):
+    """Backward for ``[B, H, N, d]`` inputs: returns (dQ, dK, dV) in float64."""
+    q, k, v, do = (_f64(x) for x in (q, k, v, do))
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = backward_head(q[b, h], k[b, h], v[b, h], do[b, h],
+                                                         causal, scale)
+    return dq, dk, dv
+
+
+def row_delta(o, do):
+    """D_i = sum_k dO_ik O_ik (equal to sum_j P_ij dP_ij because O = P V)."""
+    return (_f64(o) * _f64(do)).sum(axis=-1)
+
+
+def backward_head_rows(q, k, v, do, rows, causal: bool, scale: float):
+    """dQ for the selected query rows of one head.
+
+    Row i of dQ needs only row i of P and dP, so this evaluates large heads a
+    few rows at a time. Same formulas as ``backward_head``.
+    """
+    q, k, v, do = (_f64(x) for x in (q, k, v, do))
+    rows = np.asarray(rows)
+    s = scale_as_f32(scale)
+    p, _, _ = safe_softmax_rows(head_scores(q, k, scale, causal, rows))
+    dp = do[rows] @ v.T
+    dd = (p * dp).sum(axis=1)
+    ds = p * (dp - dd[:, None])
+    return s * (ds @ k)
+
+
+def backward_head_cols(q, k, v, do, cols, causal: bool, scale: float, chunk: int = 1024):
+    """(dK, dV) for the selected key rows of one head.
+
+    Column j of P needs every row's normaliser, so all rows are visited in
+    chunks of ``chunk`` queries (row-local softmax, so chunking changes no
+    value); only the selected columns of dS and P are kept.
+    """
+    q, k, v, do = (_f64(x) for x in (q, k, v, do))
+    cols = np.asarray(cols)
+    s = scale_as_f32(scale)
+    n = q.shape[0]
+    dk = np.zeros((cols.size, q.shape[1]))
+    dv = np.zeros((cols.size, v.shape[1]))
+    for r0 in range(0, n, chunk):
+        rows = np.arange(r0, min(n, r0 + chunk))
+        p, _, _ = safe_softmax_rows(head_scores(q, k, scale, causal, rows))
+        dp = do[rows] @ v.T
+        dd = (p * dp).sum(axis=1)
+        ds_cols = p[:, cols] * (dp[:, cols] - dd[:, None])
+        dv += p[:, cols].T @ do[rows]
+        dk += s * (ds_cols.T @ q[rows])
+    return dk, dv
+
+
+def online_forward_head(q, k, v, causal: bool, scale: float, block_edges):
+    """Diagnostic: the online recurrence over key blocks ([LIB] "online softmax").
+
+    ``block_edges`` is an increasing list of key offsets starting at 0 and
+    ending at N (any partition, ragged allowed). Per block: new running max,
+    rescale factor exp(m_old - m_new) applied to l and to the partial output,
+    add this block's exp(x - m_new) terms; divide by l at the end. Used only to
+    check that the two-pass definition and the recurrence agree.
+    """
+    q, k, v = (_f64(x) for x in (q, k, v))
+    n = q.shape[0]
+    m = np.full(n, -np.inf)
+    l = np.zeros(n)
+    acc = np.zeros((n, v.shape[1]))
+    for j0, j1 in zip(block_edges[:-1], block_edges[1:]):
+        s = scale_as_f32(scale) * (q @ k[j0:j1].T)
+        if causal:
+            keys = np.arange(j0, j1)
+            s[keys[None, :] > np.arange(n)[:, None]] = -np.inf
+        m_new = np.maximum(m, s.max(axis=1))
+        # rows whose running max is still -inf have seen no visible key yet
+        alpha = np.where(np.isneginf(m_new), 0.0, np.exp(m - np.where(np.isneginf(m_new), 0.0, m_new)))
+        p = np.where(np.isneginf(m_new)[:, None], 0.0,
+                     np.exp(s - np.where(np.isneginf(m_new), 0.0, m_new)[:, None]))
+        l = alpha * l + p.sum(axis=1)
+        acc = alpha[:, None] * acc + p @ v[j0:j1]
+        m = m_new
+    return acc / l[:, None], m + np.log(l)
+
+
+# ---------------------------------------------------------------- metrics
+def rel_rms(x, ref) -> float:
+    """||x - ref||_2 / ||ref||_2 over the whole tensor."""
+    x = _f64(x)
+    ref = _f64(ref)
+    return float(np.linalg.norm((x - ref).ravel()) / np.linalg.norm(ref.ravel()))
+
+
+def max_abs(x, ref) -> float:
+    return float(np.max(np.abs(_f64(x) - _f64(ref)))) if np.size(ref) else 0.0

@@ -1,0 +1,164 @@
+// C ABI of the attention library: argument validation, device check, dispatch.
+// Validation runs entirely on the host and touches no HIP API, so a bad call
+// returns its status on any machine; the device check is the last step before
+// a launch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_DEVICE;
+  int st = g_device_ok[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t p;
+    if (hipGetDeviceProperties(&p, dev) != hipSuccess) return FA_ERR_DEVICE;
+    st = (std::strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_ok[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? FA_OK : FA_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range span(const void* p, size_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Every output range must be disjoint from every other range.
+bool any_alias(const Range* outs, int nout, const Range* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+bool shape_ok(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return false;
+  const double elems = (double)B * H * N * d;
+  return elems < 1099511627776.0 && (double)B * H < 2147483647.0 && N <= (1 << 24);
+}
+
+bool scalars_ok(int causal, float scale) {
+  return (causal == 0 || causal == 1) && std::isfinite(scale) && scale > 0.f;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: B, H or N out of range";
+    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: unsupported head dim";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointer not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace NULL, misaligned or too small";
+    case FA_ERR_DEVICE: return "FA_ERR_DEVICE: no gfx950 device current";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps another tensor";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
+    case FA_ERR_ARG: return "FA_ERR_ARG: causal must be 0/1 and scale finite and positive";
+    default: return "FA_ERR_UNKNOWN";
+  }
+}
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+int fa_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+           int B, int H, int N, int d, int causal, float scale, void* stream) {
+  if (!scalars_ok(causal, scale)) return FA_ERR_ARG;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!shape_ok(B, H, N, d)) return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
+  const Range ins[3] = {span(q, tb), span(k, tb), span(v, tb)};
+  const Range outs[2] = {span(o, tb), span(lse, lb)};
+  if (any_alias(outs, 2, ins, 3)) return FA_ERR_ALIAS;
+  if (int st = check_device()) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal, scale, stream};
+  return fa::launch_fwd(a) ? FA_ERR_LAUNCH : FA_OK;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if ((d != 64 && d != 128) || !shape_ok(B, H, N, d)) return 0;
+  return fa::bwd_dq_acc_bytes(B, H, N, d) + fa::bwd_delta_bytes(B, H, N);
+}
+
+int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+           const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+           int B, int H, int N, int d, int causal, float scale, void* ws, size_t ws_bytes,
+           void* stream) {
+  if (!scalars_ok(causal, scale)) return FA_ERR_ARG;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!shape_ok(B, H, N, d)) return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
+      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGN;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+  if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
+  const Range ins[6] = {span(q, tb), span(k, tb), span(v, tb), span(o, tb), span(dO, tb), span(lse, lb)};
+  const Range outs[4] = {span(dq, tb), span(dk, tb), span(dv, tb), span(ws, need)};
+  if (any_alias(outs, 4, ins, 6)) return FA_ERR_ALIAS;
+  if (int st = check_device()) return st;
+  float* dq_acc = (float*)ws;
+  float* delta = (float*)((char*)ws + fa::bwd_dq_acc_bytes(B, H, N, d));
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dq_acc, delta, B, H, N, d, causal, scale, stream};
+  return fa::launch_bwd(a) ? FA_ERR_LAUNCH : FA_OK;
+}
+
+int fa_quant_fp8(const uint16_t* x, uint8_t* x8, float* scales, const int8_t* signs_or_null,
+                 int B, int H, int N, int d, void* stream) {
+  if (!x || !x8 || !scales) return FA_ERR_NULL;
+  if ((d != 64 && d != 128) || (signs_or_null && d != 128)) return FA_ERR_HEADDIM;
+  if (!shape_ok(B, H, N, d)) return FA_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(x8) || !aligned16(scales)) return FA_ERR_ALIGN;
+  const size_t n = (size_t)B * H * N * d, nb = (size_t)B * H * ((N + 127) / 128) * 4;
+  const Range ins[2] = {span(x, 2 * n), span(signs_or_null, signs_or_null ? 128 : 0)};
+  const Range outs[2] = {span(x8, n), span(scales, nb)};
+  if (any_alias(outs, 2, ins, signs_or_null ? 2 : 1)) return FA_ERR_ALIAS;
+  if (int st = check_device()) return st;
+  fa::QuantArgs a{x, x8, scales, signs_or_null, B, H, N, d, stream};
+  return fa::launch_quant_fp8(a) ? FA_ERR_LAUNCH : FA_OK;
+}
+
+int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+               const float* k_scale, const float* v_scale, uint16_t* o, float* lse,
+               int B, int H, int N, int d, int causal, float scale, void* stream) {
+  if (!scalars_ok(causal, scale)) return FA_ERR_ARG;
+  if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o || !lse) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!shape_ok(B, H, N, d)) return FA_ERR_SHAPE;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(q_scale) ||
+      !aligned16(k_scale) || !aligned16(v_scale) || !aligned16(o) || !aligned16(lse))
+    return FA_ERR_ALIGN;
+  const size_t n = (size_t)B * H * N * d, nb = (size_t)B * H * ((N + 127) / 128) * 4;
+  const Range ins[6] = {span(q8, n), span(k8, n), span(v8, n), span(q_scale, nb), span(k_scale, nb),
+                        span(v_scale, nb)};
+  const Range outs[2] = {span(o, 2 * n), span(lse, (size_t)B * H * N * 4)};
+  if (any_alias(outs, 2, ins, 6)) return FA_ERR_ALIAS;
+  if (int st = check_device()) return st;
+  fa::Fp8FwdArgs a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, causal, scale, stream};
+  return fa::launch_fwd_fp8(a) ? FA_ERR_LAUNCH : FA_OK;
+}
+
+}  // extern "C"

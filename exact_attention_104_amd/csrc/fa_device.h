@@ -1,0 +1,87 @@
+// Device-side helpers shared by the gfx950 attention kernels: vector types,
+// MFMA wrappers, LDS transpose reads, lane exchange, bf16/fp8 conversion.
+//
+// Register layouts used throughout (measured on gfx950 with a layout probe):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[m = l%32][k = 8*(l/32) + j], j = 0..7 (one bf16x8)
+//     B: lane l holds B[k = 8*(l/32) + j][n = l%32]
+//     D: lane l, element i holds D[m = 8*(i/4) + 4*(l/32) + i%4][n = l%32]
+//   ds_read_b64_tr_b16: in each group of 16 lanes, lane i supplies the address
+//     of 4 consecutive 16-bit values; the group reads a 4 x 16 block whose row r
+//     comes from lanes 4r..4r+3, and lane i receives column i (rows 0..3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define FA_LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// e4m3 x e4m3 -> fp32, 32x32x64; A/B: 32 bytes per lane. Any k permutation that
+// is the same for A and B gives the same product, so only the pairing matters.
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS_PTR(i16x4, p));
+}
+
+__device__ __forceinline__ i32x2 lds_read_tr8(const void* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(FA_LDS_PTR(i32x2, p));
+}
+
+// Value of x held by lane l ^ 32 (the other half of the wave), via v_permlane32_swap.
+__device__ __forceinline__ float other_half(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  // r[0] = (lanes <32: own, >=32: lane-32), r[1] = (lanes <32: lane+32, >=32: own)
+  const bool upper = (threadIdx.x & 32) != 0;
+  return __builtin_bit_cast(float, upper ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+// XOR swizzles of 16-byte chunks inside an LDS row of a [rows][D] bf16 tile.
+// K tile: read as 32 rows x one chunk per 16 lanes -> chunk ^ f(row) spreads
+// 16 consecutive rows over 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+// V tile: read transposed, 4 rows x 4 chunks per 16-lane group.
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+}  // namespace fa

@@ -1,0 +1,74 @@
+// Host-side launch interface between the C ABI (fa_api.hip) and the kernel
+// files. Arguments arrive here already validated.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int B, H, N, d, causal;
+  float scale;
+  void* stream;
+};
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dO;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dq_acc;  // workspace: fp32 [B, H, N, d]
+  float* delta;   // workspace: fp32 [B, H, N]
+  int B, H, N, d, causal;
+  float scale;
+  void* stream;
+};
+
+struct QuantArgs {
+  const uint16_t* x;
+  uint8_t* x8;
+  float* scales;
+  const int8_t* signs;  // NULL: no rotation
+  int B, H, N, d;
+  void* stream;
+};
+
+struct Fp8FwdArgs {
+  const uint8_t* q8;
+  const uint8_t* k8;
+  const uint8_t* v8;
+  const float* qs;
+  const float* ks;
+  const float* vs;
+  uint16_t* o;
+  float* lse;
+  int B, H, N, d, causal;
+  float scale;
+  void* stream;
+};
+
+// Each returns 0 on a successful launch, nonzero if hipGetLastError reports one.
+int launch_fwd(const FwdArgs& a);
+int launch_bwd(const BwdArgs& a);
+int launch_quant_fp8(const QuantArgs& a);
+int launch_fwd_fp8(const Fp8FwdArgs& a);
+
+// Workspace layout of the backward pass (256-byte aligned pieces).
+inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline size_t bwd_dq_acc_bytes(int B, int H, int N, int d) {
+  return round256((size_t)B * H * N * d * sizeof(float));
+}
+inline size_t bwd_delta_bytes(int B, int H, int N) { return round256((size_t)B * H * N * sizeof(float)); }
+
+}  // namespace fa

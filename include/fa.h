@@ -1,0 +1,136 @@
+/*
+ * fa.h — C ABI of the MI355X (gfx950) exact-attention library (libfa_mi355x.so).
+ *
+ * Exact scaled-dot-product attention computed the FlashAttention way: score
+ * tiles S = Q K^T are formed and consumed on chip, the softmax is applied
+ * online with a running (m, l) state, the output is normalised once at the
+ * end, a per-row logsumexp is saved, and the backward pass recomputes P from it.
+ *
+ * Sources (web pages):
+ *   [LIB] "FlashAttention v1/v2/v3/v4: the librarian who never clears the desk"
+ *   [HUB] research-hub concept page "FlashAttention"
+ *   [LIN] "The FlashAttention lineage — FA1 / FA2 / FA3 / FA4"
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Tensors are [B, H, N, d] row-major (d fastest), the (batch, heads, tokens,
+ *   head dim) order of PyTorch's scaled_dot_product_attention. Per-row vectors
+ *   (LSE) are [B, H, N] float32. bf16 values travel as their uint16_t bits.
+ * - Every tensor pointer is a DEVICE pointer owned by the caller, 16-byte
+ *   aligned, on the current HIP device. The library never allocates, frees or
+ *   keeps device memory; the backward workspace comes from the caller.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream). All
+ *   calls are asynchronous on that stream; a device fault surfaces at the
+ *   caller's next synchronisation.
+ * - Supported: d in {64, 128}; B, H, N >= 1 with B*H*N*d < 2^40; causal in {0, 1};
+ *   scale finite and > 0. Causal means query i sees key j iff j <= i.
+ * - Arguments are validated before anything is launched. On error nothing is
+ *   written and a status below is returned; the library never prints or aborts.
+ * - Forward calls are bitwise deterministic for fixed inputs and shape.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,     /* B, H or N < 1, or the tensor is too large */
+  FA_ERR_HEADDIM = 3,   /* d not supported (or rotation requested with d != 128) */
+  FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE = 5, /* backward workspace NULL, misaligned or too small */
+  FA_ERR_DEVICE = 6,    /* no HIP device, or the current device is not gfx950 */
+  FA_ERR_ALIAS = 7,     /* an output overlaps an input or another output */
+  FA_ERR_LAUNCH = 8,    /* the kernel launch failed (hipGetLastError) */
+  FA_ERR_ARG = 9        /* causal not 0/1, or scale not finite and positive */
+};
+
+/* Human-readable name of a status (static string, never NULL). */
+const char* fa_status_string(int status);
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+/*
+ * Forward: O = softmax(scale * Q K^T [+ causal mask]) V and
+ * LSE_i = log sum_j exp(scale * q_i . k_j) over the visible keys (natural log).
+ * [HUB] "How it works" (definition, fusion, saved L_i = m_i + log l_i);
+ * [LIB] "The trick that made it all possible: online softmax" (recurrence);
+ * [LIN] "FA2 (2023)" (sequence-parallel grid, split-Q, deferred division).
+ *   q, k, v : in,  bf16 [B, H, N, d]
+ *   o       : out, bf16 [B, H, N, d] (round to nearest even from fp32)
+ *   lse     : out, fp32 [B, H, N]
+ */
+int fa_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+           int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: an fp32 dQ accumulator
+ * [B, H, N, d] and the fp32 row vector D = rowsum(dO o O) [B, H, N], each
+ * rounded up to 256 bytes. Returns 0 for invalid shapes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward by recomputation: P_ij = exp(scale q_i.k_j - LSE_i) is rebuilt tile
+ * by tile from the saved LSE ([HUB] "How it works"; [LIB] "FA1 — changing the
+ * order of the operations"); dV = P^T dO, dP = dO V^T, D = rowsum(dO o O),
+ * dS = P o (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ *   q, k, v, o, dO : in, bf16 [B, H, N, d] (o and lse as produced by fa_fwd)
+ *   lse            : in, fp32 [B, H, N]
+ *   dq, dk, dv     : out, bf16 [B, H, N, d]
+ *   ws, ws_bytes   : caller-owned device workspace, >= fa_bwd_workspace_bytes,
+ *                    256-byte aligned; its contents on entry are ignored.
+ * dK and dV are deterministic; dQ is accumulated with fp32 atomics and may
+ * differ in the last bits between runs.
+ */
+int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+           const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+           int B, int H, int N, int d, int causal, float scale, void* ws, size_t ws_bytes,
+           void* stream);
+
+/*
+ * FP8 input path ([LIB] "FA3 — the Hopper moment", pillar 3; [LIN] "FA3
+ * (2024)", idea 3): optional random-sign Hadamard rotation along d, then block
+ * quantisation to OCP E4M3FN with one fp32 scale per 128 token rows of a
+ * (batch, head).
+ *   x             : in,  bf16 [B, H, N, d]
+ *   x8            : out, e4m3 codes [B, H, N, d]
+ *   scales        : out, fp32 [B, H, ceil(N / 128)]; scale = fl32(amax / 448),
+ *                   1 for an all-zero block
+ *   signs_or_null : in, device int8 [128] of +-1 (rotation x' = H_128 (s o x) /
+ *                   sqrt(128), d must be 128), or NULL for no rotation
+ * Codes: e4m3_rne_saturating(fl32(x' * fl32(448 / amax))). Rotation order:
+ * multiply by s, butterflies (a, b) -> (a + b, a - b) at strides 1, 2, ..., 64,
+ * multiply by fl32(1 / sqrt(128)), all in fp32.
+ */
+int fa_quant_fp8(const uint16_t* x, uint8_t* x8, float* scales, const int8_t* signs_or_null,
+                 int B, int H, int N, int d, void* stream);
+
+/*
+ * FP8 forward on block-quantised inputs (as produced by fa_quant_fp8; Q and K
+ * rotated with the same signs or not at all, V never rotated). Computes the
+ * forward above on the dequantised values x8 * scale: e4m3 MFMA for Q K^T and
+ * P V with fp32 accumulation; P is quantised to e4m3 for the P V product.
+ *   q8, k8, v8                  : in, e4m3 [B, H, N, d]
+ *   q_scale, k_scale, v_scale   : in, fp32 [B, H, ceil(N / 128)]
+ *   o                           : out, bf16 [B, H, N, d]
+ *   lse                         : out, fp32 [B, H, N]
+ */
+int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+               const float* k_scale, const float* v_scale, uint16_t* o, float* lse,
+               int B, int H, int N, int d, int causal, float scale, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,106 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and rejects bad arguments before touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import exact_attention_104_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+P = 0x10000  # a 16-byte aligned, non-null fake address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def declared_status_codes():
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"(FA_[A-Z_]+)\s*=\s*(\d+)", text)}
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    lib = fa.load_library()
+    names = declared_functions()
+    assert names == sorted(fa.SIGNATURES)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert fa.abi_version() == 1
+    codes = declared_status_codes()
+    assert codes["FA_OK"] == 0 and len(codes) == 10
+    for name, val in codes.items():
+        assert fa.FA_STATUS[val] == name
+        assert fa.status_string(val).startswith(name)
+    assert fa.status_string(1234) == "FA_ERR_UNKNOWN"
+
+
+def test_workspace_bytes():
+    lib = fa.load_library()
+    n = lib.fa_bwd_workspace_bytes(2, 16, 4096, 128)
+    assert n == 2 * 16 * 4096 * 128 * 4 + 2 * 16 * 4096 * 4
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 64) == 768 + 256  # pieces rounded to 256 B
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 96) == 0
+    assert lib.fa_bwd_workspace_bytes(0, 1, 3, 64) == 0
+
+
+def _fwd(**kw):
+    a = dict(q=P, k=P + 0x100000, v=P + 0x200000, o=P + 0x300000, lse=P + 0x400000,
+             B=1, H=1, N=64, d=64, causal=0, scale=0.125, stream=None)
+    a.update(kw)
+    return fa.load_library().fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                                    a["d"], a["causal"], a["scale"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(causal=2), 9), (dict(scale=float("nan")), 9), (dict(scale=0.0), 9), (dict(scale=-1.0), 9),
+    (dict(q=None), 1), (dict(lse=None), 1),
+    (dict(d=96), 3), (dict(d=256), 3),
+    (dict(B=0), 2), (dict(N=0), 2), (dict(H=-1), 2), (dict(N=(1 << 24) + 1), 2),
+    (dict(k=P + 8), 4), (dict(lse=P + 0x400004), 4),
+    (dict(o=P), 7), (dict(lse=P + 0x100000 + 64), 7), (dict(o=P + 0x200000 + 0x10), 7),
+])
+def test_fwd_rejects_bad_arguments(kw, status):
+    assert _fwd(**kw) == status
+
+
+def test_bwd_quant_fp8_reject_bad_arguments():
+    lib = fa.load_library()
+    ws = 0x40000000
+    good = [P + i * 0x100000 for i in range(9)]
+    args = good + [1, 1, 64, 64, 1, 0.125, ws, lib.fa_bwd_workspace_bytes(1, 1, 64, 64), None]
+    bad = list(args)
+    bad[15] = ws + 16                   # misaligned workspace
+    assert lib.fa_bwd(*bad) == 5
+    bad = list(args)
+    bad[16] = 100                       # too small
+    assert lib.fa_bwd(*bad) == 5
+    bad = list(args)
+    bad[6] = good[0]                    # dq aliases q
+    assert lib.fa_bwd(*bad) == 7
+    bad = list(args)
+    bad[5] = None
+    assert lib.fa_bwd(*bad) == 1
+    # quantiser: rotation needs d = 128; NULL output; misalignment
+    assert lib.fa_quant_fp8(P, P + 0x100000, P + 0x200000, P + 0x300000, 1, 1, 64, 64, None) == 3
+    assert lib.fa_quant_fp8(P, None, P + 0x200000, None, 1, 1, 64, 64, None) == 1
+    assert lib.fa_quant_fp8(P, P + 0x100000 + 4, P + 0x200000, None, 1, 1, 64, 64, None) == 4
+    assert lib.fa_quant_fp8(P, P + 0x40, P + 0x200000, None, 1, 1, 64, 64, None) == 7
+    f8 = [P + i * 0x100000 for i in range(8)]
+    assert lib.fa_fwd_fp8(*f8[:7], None, 1, 1, 64, 64, 0, 0.125, None) == 1
+    assert lib.fa_fwd_fp8(*f8, 1, 1, 64, 80, 0, 0.125, None) == 3
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="valid-looking fake pointers must never reach a GPU")
+def test_no_device_is_reported_after_validation():
+    assert _fwd() == 6

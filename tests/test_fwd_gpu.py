@@ -1,0 +1,92 @@
+"""fa_fwd (bf16) against the fp64 oracle, through the C ABI, on the GPU."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from gpu_util import LSE_ABS, O_MAX_ABS, O_REL_RMS, inputs_on_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(o, lse, o_ref, lse_ref, tag=""):
+    o = np.asarray(o, np.float64)
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), tag
+    mx = A.max_abs(o, o_ref)
+    rr = A.rel_rms(o, o_ref)
+    le = A.max_abs(lse, lse_ref)
+    print("%s max_abs=%.3e rel_rms=%.3e lse_abs=%.3e" % (tag, mx, rr, le), flush=True)
+    assert mx <= O_MAX_ABS and rr <= O_REL_RMS and le <= LSE_ABS, tag
+
+
+def _full(gpu, B, H, N, d, causal, seed):
+    host, dev = inputs_on_device(B, H, N, d, seed)
+    o, lse = gpu.fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = A.forward(host["q"], host["k"], host["v"], causal, 1.0 / math.sqrt(d))
+    _check(to_host(o), to_host(lse), o_ref, lse_ref, "B%d H%d N%d d%d c%d" % (B, H, N, d, causal))
+    return host, dev, o, lse
+
+
+def test_fwd_small_noncausal(gpu):
+    _full(gpu, 1, 2, 256, 64, False, 1)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_n2048_d64(gpu, causal):
+    _full(gpu, 4, 16, 2048, 64, causal, 2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 100, 129, 255, 300, 513])
+def test_fwd_edge_lengths(gpu, N, d, causal):
+    _full(gpu, 1, 3, N, d, causal, 1000 + N)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_several_tiles_d(gpu, d):
+    _full(gpu, 2, 3, 1000, d, True, 77)
+
+
+def test_fwd_n8192_d128_causal_sampled(gpu):
+    """Full-size workload (2 x 16 x 8192 x 128, causal): sampled rows vs the oracle,
+    plus properties of every output."""
+    B, H, N, d = 2, 16, 8192, 128
+    host, dev = inputs_on_device(B, H, N, d, 3)
+    o, lse = gpu.fwd(dev["q"], dev["k"], dev["v"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 255, 256, 4095, 4096, 8191],
+                                     np.random.default_rng(0).integers(0, N, 40)]))
+    o_h = to_host(o)
+    lse_h = to_host(lse)
+    for b, h in ((0, 0), (1, 15), (0, 7)):
+        o_ref, lse_ref = A.forward_head(host["q"][b, h], host["k"][b, h], host["v"][b, h], True,
+                                        1.0 / math.sqrt(d), rows)
+        _check(o_h[b, h, rows], lse_h[b, h, rows], o_ref, lse_ref, "n8192 head (%d,%d)" % (b, h))
+    # causal row 0 sees only key 0: O_0 = V_0 exactly
+    assert torch.equal(o[:, :, 0], dev["v"][:, :, 0])
+
+
+def test_fwd_deterministic_and_covers_outputs(gpu):
+    B, H, N, d = 2, 4, 777, 128
+    host, dev = inputs_on_device(B, H, N, d, 5)
+    o1 = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    l1 = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    gpu.fwd(dev["q"], dev["k"], dev["v"], causal=True, out=o1, lse=l1)
+    o2, l2 = gpu.fwd(dev["q"], dev["k"], dev["v"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1).all() and torch.isfinite(l1).all()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fwd_scale_argument(gpu):
+    host, dev = inputs_on_device(1, 2, 300, 64, 9)
+    o, lse = gpu.fwd(dev["q"], dev["k"], dev["v"], causal=False, scale=0.37)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = A.forward(host["q"], host["k"], host["v"], False, 0.37)
+    _check(to_host(o), to_host(lse), o_ref, lse_ref, "scale 0.37")

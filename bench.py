@@ -1,0 +1,240 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+One step runs every kernel of the path once on the headline workload
+(B=2, H=16, N=8192, d=128, causal), inputs already resident in HBM:
+  fa_fwd (bf16)  ->  fa_bwd (bf16, recomputing P from the saved LSE)
+  ->  fa_quant_fp8 on Q, K (random-sign Hadamard rotation) and V  ->  fa_fwd_fp8.
+Kernels that are not built yet are left out of the step and listed as such.
+
+Prints ONE JSON line on stdout: whole-step algorithmic TFLOP/s (causal
+attention FLOPs: forward 4 B H N^2 d / 2, backward 2.5x that, fp8 forward as
+forward), the per-kernel breakdown with % of the MI355X dense MFMA peak, the
+roofline of the dominant kernel (timed with HIP events on the stream it runs
+on), and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOPS (bf16, causal, d=128, N=8k) + % of MFMA peak, 1 GPU"
+PEAK_BF16 = 2516.6   # TFLOP/s, dense MFMA, 256 CUs x 4096 FLOP/clk x 2.4 GHz
+PEAK_FP8 = 5033.2    # TFLOP/s
+PEAK_HBM = 8000.0    # GB/s
+B, H, N, D = 2, 16, 8192, 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_flops(b, h, n, d, causal=True):
+    f = 4.0 * b * h * n * n * d
+    return f / 2 if causal else f
+
+
+def fwd_bytes(b, h, n, d, elt=2):
+    # Q, K, V in and O out (elt bytes each) plus the fp32 LSE
+    return 4.0 * b * h * n * d * elt + 4.0 * b * h * n
+
+
+def bwd_bytes(b, h, n, d):
+    # reads Q, K, V, O, dO (bf16) and LSE; writes dQ, dK, dV (bf16); D written once, read once
+    return 8.0 * b * h * n * d * 2 + 4.0 * b * h * n * 3
+
+
+def quant_bytes(b, h, n, d):
+    return b * h * n * d * (2 + 1) + 4.0 * b * h * ((n + 127) // 128)
+
+
+def cpu_baseline(sample_heads: int):
+    """The fp64 oracle (as it stands) on `sample_heads` heads of the bf16
+    workload: one forward and one backward per head."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import fa_inputs
+    from oracle import attention as A
+
+    rng = np.random.Generator(np.random.PCG64(3))
+    q, k, v, do = (rng.standard_normal((sample_heads, N, D), dtype=np.float32) for _ in range(4))
+    q, k, v, do = (fa_inputs.to_bf16_values(x) for x in (q, k, v, do))
+    scale = 1.0 / math.sqrt(D)
+    t0 = time.perf_counter()
+    for i in range(sample_heads):
+        A.forward_head(q[i], k[i], v[i], True, scale)
+        A.backward_head(q[i], k[i], v[i], do[i], True, scale)
+    dt = time.perf_counter() - t0
+    flops = 3.5 * fwd_flops(1, sample_heads, N, D)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "fp64 forward + backward by definition on %d of the %d heads of the "
+                      "B=%d H=%d N=%d d=%d causal workload (%.1f s); algorithmic causal FLOPs / wall time"
+                      % (sample_heads, B * H, B, H, N, D, dt),
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(the (batch, head) pairs would shard with no communication)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_104_amd as fa
+    import fa_inputs
+
+    fa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating inputs B=%d H=%d N=%d d=%d" % (B, H, N, D))
+    host = fa_inputs.attention_inputs(B, H, N, D, seed=3, with_do=True)
+    q, k, v, do = (torch.from_numpy(host[n]).to(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do"))
+    h8 = fa_inputs.attention_inputs(B, H, N, D, seed=5, outliers=True)
+    q5, k5, v5 = (torch.from_numpy(h8[n]).to(torch.bfloat16).to(dev) for n in ("q", "k", "v"))
+    signs = torch.from_numpy(fa_inputs.hadamard_signs()).to(dev)
+    del host, h8
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, D), dtype=torch.uint8, device=dev)
+
+    # which kernels exist
+    def available(fn):
+        try:
+            fn()
+            torch.cuda.synchronize()
+            return True
+        except fa.FAError as e:
+            log("left out of the step: %s" % e)
+            return False
+
+    have_fwd = available(lambda: fa.fwd(q, k, v, causal=True, out=o, lse=lse))
+    have_bwd = have_fwd and available(lambda: fa.bwd(q, k, v, o, do, lse, causal=True, workspace=ws))
+    have_q8 = available(lambda: fa.quant_fp8(q5, signs))
+    have_f8 = False
+    if have_q8:
+        q8, qs = fa.quant_fp8(q5, signs)
+        k8, ks = fa.quant_fp8(k5, signs)
+        v8, vs = fa.quant_fp8(v5, None)
+        have_f8 = available(lambda: fa.fwd_fp8(q8, k8, v8, qs, ks, vs, causal=True))
+
+    stream = torch.cuda.current_stream()
+    kernels = []  # (name, callable, flops, bytes, peak)
+    if have_fwd:
+        kernels.append(("fa_fwd", lambda: fa.fwd(q, k, v, causal=True, out=o, lse=lse),
+                        fwd_flops(B, H, N, D), fwd_bytes(B, H, N, D), PEAK_BF16))
+    if have_bwd:
+        kernels.append(("fa_bwd", lambda: fa.bwd(q, k, v, o, do, lse, causal=True, workspace=ws),
+                        2.5 * fwd_flops(B, H, N, D), bwd_bytes(B, H, N, D), PEAK_BF16))
+    if have_q8:
+        def quant3():
+            fa.quant_fp8(q5, signs)
+            fa.quant_fp8(k5, signs)
+            fa.quant_fp8(v5, None)
+        kernels.append(("fa_quant_fp8 x3", quant3, 0.0, 3 * quant_bytes(B, H, N, D), None))
+    if have_f8:
+        kernels.append(("fa_fwd_fp8", lambda: fa.fwd_fp8(q8, k8, v8, qs, ks, vs, causal=True),
+                        fwd_flops(B, H, N, D), fwd_bytes(B, H, N, D, 1), PEAK_FP8))
+    if not kernels:
+        raise RuntimeError("no kernel of the path is available")
+
+    for _ in range(args.warmup):
+        for _, fn, *_r in kernels:
+            fn()
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in kernels] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        for i, (_, fn, *_r) in enumerate(kernels):
+            ev[s][i][0].record(stream)
+            fn()
+            ev[s][i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+
+    breakdown = {}
+    step_flops = 0.0
+    dom = None
+    for i, (name, _, flops, nbytes, peak) in enumerate(kernels):
+        times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        avg = float(np.mean(times))
+        ent = {"ms_avg": avg, "ms_min": float(np.min(times))}
+        if flops:
+            ent["tflops"] = flops / (avg * 1e-3) / 1e12
+            ent["pct_of_peak"] = 100.0 * ent["tflops"] / peak
+        ent["gbps"] = nbytes / (avg * 1e-3) / 1e9
+        breakdown[name] = ent
+        step_flops += flops
+        if dom is None or avg > breakdown[dom[0]]["ms_avg"]:
+            dom = (name, flops, nbytes, peak)
+
+    name, flops, nbytes, peak = dom
+    if peak:
+        achieved = breakdown[name]["tflops"]
+        roofline = {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": peak,
+                    "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                    "per_launch_flops": flops, "avg_launch_ms": breakdown[name]["ms_avg"]}
+    else:
+        achieved = breakdown[name]["gbps"]
+        roofline = {"kernel": name, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM,
+                    "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None}
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on %d heads" % args.cpu_heads)
+        cpu = cpu_baseline(args.cpu_heads)
+
+    dtypes = ["bf16"] + (["e4m3"] if have_f8 else [])
+    out = {
+        "metric": METRIC,
+        "value": step_flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "+".join(dtypes),
+        "data": "synthetic",
+        "config": {"workload": "causal attention B=2 H=16 N=8192 d=128 (bf16; fp8 leg with 0.1% x20 "
+                               "outliers, Hadamard-rotated Q/K)",
+                   "B": B, "H": H, "N": N, "d": D, "causal": True,
+                   "step": [k[0] for k in kernels]},
+        "breakdown": breakdown,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,80 @@
+"""fa_bwd (bf16, recomputation from the saved LSE) against the fp64 oracle."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from gpu_util import GRAD_REL_RMS, inputs_on_device, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(gpu, B, H, N, d, causal, seed):
+    host, dev = inputs_on_device(B, H, N, d, seed, with_do=True)
+    o, lse = gpu.fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+    dq, dk, dv = gpu.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=causal)
+    torch.cuda.synchronize()
+    return host, dev, (o, lse), (dq, dk, dv)
+
+
+def _check_grads(got, ref, tag):
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        g = np.asarray(g, np.float64)
+        assert np.isfinite(g).all(), (tag, name)
+        if np.linalg.norm(np.ravel(r)) == 0.0:
+            # exactly zero by definition (a single visible key: dS = P (dP - D) = 0);
+            # the kernel's D and dP differ only by summation order
+            print("%s %s max_abs=%.3e (zero reference)" % (tag, name, np.abs(g).max()), flush=True)
+            assert np.abs(g).max() <= 1e-4, (tag, name)
+            continue
+        e = A.rel_rms(g, r)
+        print("%s %s rel_rms=%.3e" % (tag, name, e), flush=True)
+        assert e <= GRAD_REL_RMS, (tag, name, e)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 17, 100, 129, 255, 300, 640])
+def test_bwd_edge_lengths(gpu, N, d, causal):
+    host, dev, _, got = _run(gpu, 1, 2, N, d, causal, 2000 + N)
+    ref = A.backward(host["q"], host["k"], host["v"], host["do"], causal, 1.0 / math.sqrt(d))
+    _check_grads([to_host(t) for t in got], ref, "N%d d%d c%d" % (N, d, causal))
+
+
+def test_bwd_n4096_d128_causal(gpu):
+    """The backward workload: B=2, H=16, N=4096, d=128, causal; O, LSE from fa_fwd."""
+    B, H, N, d = 2, 16, 4096, 128
+    host, dev, _, got = _run(gpu, B, H, N, d, True, 4)
+    got = [to_host(t) for t in got]
+    ref = A.backward(host["q"], host["k"], host["v"], host["do"], True, 1.0 / math.sqrt(d))
+    _check_grads(got, ref, "bwd n4096")
+
+
+def test_bwd_n8192_d128_causal_sampled(gpu):
+    """N = 8192 (the headline backward shape): sampled dQ rows and dK/dV rows of two heads."""
+    B, H, N, d = 2, 16, 8192, 128
+    host, dev, _, got = _run(gpu, B, H, N, d, True, 3)
+    dq, dk, dv = (to_host(t) for t in got)
+    for t in (dq, dk, dv):
+        assert np.isfinite(t).all()
+    idx = np.unique(np.concatenate([[0, 1, 127, 128, 4095, 8190, 8191],
+                                    np.random.default_rng(1).integers(0, N, 16)]))
+    scale = 1.0 / math.sqrt(d)
+    for b, h in ((0, 0), (1, 9)):
+        args = (host["q"][b, h], host["k"][b, h], host["v"][b, h], host["do"][b, h])
+        rq = A.backward_head_rows(*args, idx, True, scale)
+        rk, rv = A.backward_head_cols(*args, idx, True, scale)
+        _check_grads([dq[b, h, idx], dk[b, h, idx], dv[b, h, idx]], [rq, rk, rv],
+                     "n8192 head (%d,%d)" % (b, h))
+
+
+def test_bwd_dk_dv_deterministic(gpu):
+    host, dev, (o, lse), (dq, dk, dv) = _run(gpu, 1, 4, 700, 128, True, 6)
+    dq2, dk2, dv2 = gpu.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    # dQ is accumulated with atomics: equal up to summation order
+    assert (dq.float() - dq2.float()).abs().max().item() <= 2e-2 * dq.float().abs().max().item()

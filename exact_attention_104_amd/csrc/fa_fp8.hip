@@ -1,6 +1,350 @@
-// fp8 path (not built yet: every call reports a launch failure).
+// fp8 (OCP e4m3) input path for gfx950: block quantiser with optional
+// random-sign Hadamard rotation, and the e4m3 MFMA forward.
+//
+// [LIB] "FA3 — the Hopper moment", pillar 3, and [LIN] "FA3 (2024)", idea 3:
+// e4m3 attention inputs, one scale per tile of rows instead of per tensor
+// (block quantisation), and an orthogonal random Hadamard-based rotation that
+// spreads outliers before quantising ("incoherent processing").
+//
+// Quantiser: one workgroup per (batch, head, 128-row block). Rotation along d
+// (d = 128): x' = H_128 (s o x) / sqrt(128) in fp32 with butterflies at
+// strides 1, 2, 4 inside a lane's 8 values and 8, 16, 32, 64 across lanes;
+// then scale = fl32(amax / 448), codes = e4m3(clamp(fl32(x' * fl32(448 / amax)))).
+//
+// Forward: as the bf16 forward (split-Q waves of 64 query rows, S^T = K Q^T
+// so lanes own queries, online exp2 softmax with conditional rescale), on
+// v_mfma_f32_32x32x64 e4m3 products with fp32 accumulation. Block scales are
+// applied after the products: S = sq * sk * (Q8 K8^T). P is quantised to e4m3
+// for the P V product with the V block scale folded in: p' = p * sv_j * R with
+// R = 256 / max_j sv_j (so p' <= 256), the row sum keeps the unscaled p, and
+// the final division removes R.
+#include "fa_device.h"
 #include "fa_internal.h"
+
 namespace fa {
-int launch_quant_fp8(const QuantArgs&) { return 1; }
-int launch_fwd_fp8(const Fp8FwdArgs&) { return 1; }
+
+// 4 floats -> 4 e4m3 bytes (RNE); the inputs are already clamped to +-448.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+template <int D, bool ROT>
+__global__ void __launch_bounds__(256)
+quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __restrict__ scales,
+             const int8_t* __restrict__ signs, int N, int nb) {
+  constexpr int LPR = D / 8;         // lanes per row, 8 values each
+  constexpr int RPP = 256 / LPR;     // rows per pass
+  constexpr int PASSES = 128 / RPP;  // passes over the 128-row block
+  __shared__ float wmax[4];
+
+  const int blk = (int)(blockIdx.x % nb);
+  const size_t bh = blockIdx.x / nb;
+  const int tid = threadIdx.x, c = tid % LPR, rr = tid / LPR;
+  const size_t base = bh * (size_t)N * D;
+
+  bool neg[8];
+  if (ROT) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) neg[j] = signs[c * 8 + j] < 0;
+  }
+  float x[PASSES][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = blk * 128 + p * RPP + rr;
+    u32x4 u = {0, 0, 0, 0};
+    if (row < N) u = *(const u32x4*)(X + base + (size_t)row * D + c * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[p][2 * j] = __builtin_bit_cast(float, u[j] << 16);
+      x[p][2 * j + 1] = __builtin_bit_cast(float, u[j] & 0xffff0000u);
+    }
+    if (ROT) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[p][j] = neg[j] ? -x[p][j] : x[p][j];
+      // strides 1, 2, 4 inside the lane
+#pragma unroll
+      for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if ((i & h) == 0) {
+            const float a = x[p][i], b = x[p][i + h];
+            x[p][i] = a + b;
+            x[p][i + h] = a - b;
+          }
+      // strides 8, 16, 32, 64 across the row's 16 lanes
+#pragma unroll
+      for (int m = 1; m < LPR; m *= 2) {
+        const bool lower = (c & m) == 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float o = __shfl_xor(x[p][i], m);
+          x[p][i] = lower ? x[p][i] + o : o - x[p][i];
+        }
+      }
+      const float inv_sqrt128 = 0x1.6a09e6p-4f;  // fl32(1 / sqrt(128))
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[p][i] = x[p][i] * inv_sqrt128;
+    }
+    if (row < N) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[p][i]));
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const bool zero = amax == 0.f;
+  const float scale = zero ? 1.f : __fdiv_rn(amax, 448.f);
+  const float factor = zero ? 1.f : __fdiv_rn(448.f, amax);
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = blk * 128 + p * RPP + rr;
+    if (row < N) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(x[p][i] * factor, -448.f), 448.f);
+      const u32x2 out = {pack_e4m3x4(v[0], v[1], v[2], v[3]), pack_e4m3x4(v[4], v[5], v[6], v[7])};
+      *(u32x2*)(X8 + base + (size_t)row * D + c * 8) = out;
+    }
+  }
+  if (tid == 0) scales[bh * nb + blk] = scale;
+}
+
+// 16-byte chunk swizzle of a [64 keys][D bytes] e4m3 tile: conflict-free for
+// 16-lane row reads and for the 8-row transposed byte reads used for V.
+template <int D>
+__device__ __forceinline__ int swz8(int row) {
+  return D == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int toff8(int row, int byte) {
+  return row * D + ((((byte >> 4) ^ swz8<D>(row))) << 4) + (byte & 15);
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
+               const float* __restrict__ QS, const float* __restrict__ KSc, const float* __restrict__ VS,
+               uint16_t* __restrict__ Og, float* __restrict__ LSEg, int BH, int N, int nqb, int nsb,
+               float scale_log2) {
+  constexpr int QW = 64, NW = 4, BR = NW * QW, BC = 64, QB = QW / 32;
+  constexpr int KS = D / 64;      // k-steps of the S product (64 bytes each)
+  constexpr int DB = D / 32;      // 32-row d blocks of O^T
+  constexpr int CHB = D / 16;     // 16-byte chunks per row
+
+  __shared__ __attribute__((aligned(16))) uint8_t sK[BC * D];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[BC * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int g = lane >> 4, i16 = lane & 15;
+
+  const int qblk = nqb - 1 - (int)(blockIdx.x / BH);
+  const int bh = (int)(blockIdx.x % BH);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const int qw0 = qblk * BR + w * QW;
+  const float* qs_h = QS + (size_t)bh * nsb;
+  const float* ks_h = KSc + (size_t)bh * nsb;
+  const float* vs_h = VS + (size_t)bh * nsb;
+
+  // R = 256 / max_j sv_j over the head, so every quantised p' = p sv_j R <= 256
+  float svm = 0.f;
+  for (int i = lane; i < nsb; i += 64) svm = fmaxf(svm, vs_h[i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) svm = fmaxf(svm, __shfl_xor(svm, o));
+  const float R = 256.f / svm;
+  const float sq = qs_h[min(qw0, N - 1) / 128];  // the wave's 64 rows share one scale block
+
+  // Q8 as the B operand of S^T = K Q^T: lane holds Q8[q][64 ks + 32 hi .. +31]
+  i32x8 qf[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw0 + qb * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      i32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+      if (row < N) {
+        const uint8_t* p = Q8 + head + (size_t)row * D + ks * 64 + hi * 32;
+        a = *(const i32x4*)p;
+        b = *(const i32x4*)(p + 16);
+      }
+      qf[qb][ks] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+  }
+
+  f32x16 acc[QB][DB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
+
+  const int kend = CAUSAL ? min(N, qblk * BR + BR) : N;
+  const int ntiles = (kend + BC - 1) / BC;
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = t * BC;
+    const float sk = ks_h[k0 / 128], sv = vs_h[k0 / 128];
+    const float ct = sq * sk * scale_log2;  // exp2 domain scale of this tile's scores
+    const float ft = sv * R;                // factor folded into p' for the P V product
+    const float tt = __log2f(ft);
+    const float inv_ft = 1.f / ft;
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < (BC * CHB) / 256; ++n) {
+      const int u = tid + 256 * n;
+      const int r = u / CHB, c = u % CHB;
+      i32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (k0 + r < N) {
+        kv = *(const i32x4*)(K8 + head + (size_t)(k0 + r) * D + c * 16);
+        vv = *(const i32x4*)(V8 + head + (size_t)(k0 + r) * D + c * 16);
+      }
+      *(i32x4*)(sK + toff8<D>(r, c * 16)) = kv;
+      *(i32x4*)(sV + toff8<D>(r, c * 16)) = vv;
+    }
+    __syncthreads();
+    if (CAUSAL && k0 > qw0 + QW - 1) continue;
+
+    // ---- S^T = K8 Q8^T (fp32 accumulation; unscaled)
+    f32x16 s[2][QB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int r = kb * 32 + l32;
+        const i32x4 a0 = *(const i32x4*)(sK + toff8<D>(r, ks * 64 + hi * 32));
+        const i32x4 a1 = *(const i32x4*)(sK + toff8<D>(r, ks * 64 + hi * 32 + 16));
+        const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_fp8_32x32x64(a, qf[qb][ks], s[kb][qb]);
+      }
+    }
+
+    // ---- online softmax; p' = p * ft quantised to e4m3 (bytes in accumulator order)
+    i32x8 pb[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qrow = qw0 + qb * 32 + l32;
+      const bool need_mask = (CAUSAL && k0 + BC - 1 > qw0 + qb * 32) || (k0 + BC > N);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
+            if ((CAUSAL && key > qrow) || key >= N) s[kb][qb][i] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][qb][i]);
+      mx = fmaxf(mx, other_half(mx));
+      const float m_new = fmaxf(m[qb], mx * ct);
+      if (__any(m_new > m[qb])) {
+        const float alpha = fast_exp2(m[qb] - m_new);
+        l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
+      }
+      m[qb] = m_new;
+      const float off = tt - m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float p[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = fast_exp2(__builtin_fmaf(s[kb][qb][4 * q4 + e], ct, off));
+            rs += p[e];
+          }
+          pb[qb][kb * 4 + q4] = (int)pack_e4m3x4(fminf(p[0], 448.f), fminf(p[1], 448.f),
+                                                 fminf(p[2], 448.f), fminf(p[3], 448.f));
+        }
+      }
+      l[qb] += rs * inv_ft;
+    }
+
+    // ---- O^T += V8^T P8^T: one 64-key MFMA per 32-row d block
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int byte = db * 32 + 16 * (g & 1) + 8 * (i16 & 1);
+      const int c = i16 >> 1;  // row of the 8 x 16 byte block this lane addresses
+      i32x8 a;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int key = 32 * (rr >> 1) + 8 * (2 * (rr & 1) + (c >> 2)) + 4 * hi + (c & 3);
+        const i32x2 t2 = lds_read_tr8(sV + toff8<D>(key, byte));
+        a[2 * rr] = t2[0];
+        a[2 * rr + 1] = t2[1];
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_fp8_32x32x64(a, pb[qb], acc[qb][db]);
+    }
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = l[qb] + other_half(l[qb]);
+    const float inv = 1.0f / (lt * R);
+    const int row = qw0 + qb * 32 + l32;
+    if (row < N) {
+      uint16_t* orow = Og + head + (size_t)row * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + 8 * g4 + 4 * hi;
+          const u32x2 pk = {pack_bf16x2(acc[qb][db][4 * g4 + 0] * inv, acc[qb][db][4 * g4 + 1] * inv),
+                            pack_bf16x2(acc[qb][db][4 * g4 + 2] * inv, acc[qb][db][4 * g4 + 3] * inv)};
+          *(u32x2*)(orow + d) = pk;
+        }
+      if (hi == 0) LSEg[(size_t)bh * N + row] = (m[qb] + __log2f(lt)) * kLn2;
+    }
+  }
+}
+
+int launch_quant_fp8(const QuantArgs& a) {
+  const int nb = (a.N + 127) / 128;
+  const dim3 grid((unsigned)(a.B * a.H * nb)), block(256);
+  hipStream_t st = (hipStream_t)a.stream;
+  if (a.d == 128) {
+    if (a.signs)
+      hipLaunchKernelGGL((quant_kernel<128, true>), grid, block, 0, st, a.x, a.x8, a.scales, a.signs, a.N, nb);
+    else
+      hipLaunchKernelGGL((quant_kernel<128, false>), grid, block, 0, st, a.x, a.x8, a.scales, a.signs, a.N, nb);
+  } else {
+    hipLaunchKernelGGL((quant_kernel<64, false>), grid, block, 0, st, a.x, a.x8, a.scales, a.signs, a.N, nb);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+template <int D, bool CAUSAL>
+static int launch_f8(const Fp8FwdArgs& a) {
+  const int nqb = (a.N + 255) / 256, nsb = (a.N + 127) / 128;
+  const int BH = a.B * a.H;
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)(nqb * BH)), dim3(256), 0,
+                     (hipStream_t)a.stream, a.q8, a.k8, a.v8, a.qs, a.ks, a.vs, a.o, a.lse, BH, a.N, nqb,
+                     nsb, a.scale * kLog2e);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+int launch_fwd_fp8(const Fp8FwdArgs& a) {
+  if (a.d == 128) return a.causal ? launch_f8<128, true>(a) : launch_f8<128, false>(a);
+  return a.causal ? launch_f8<64, true>(a) : launch_f8<64, false>(a);
+}
+
 }  // namespace fa

@@ -91,7 +91,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=12)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "

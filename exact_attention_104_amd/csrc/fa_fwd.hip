@@ -2,11 +2,11 @@
 //
 // Method ([HUB] "How it works"; [LIB] "The trick that made it all possible:
 // online softmax"; [LIN] "FA2 (2023)"): one workgroup per (batch, head,
-// Q-block); every wavefront owns its own query rows (split-Q), streams K/V
-// tiles through LDS, forms the score tile on chip with bf16 MFMA (fp32
-// accumulation), keeps the running max m and sum l per query in registers,
-// rescales the output accumulator only when some row's max changed, and
-// divides by l once at the end, saving LSE = m + log l.
+// 256-row Q-block); each of its eight wavefronts owns 32 query rows
+// (split-Q), streams 64-key K/V tiles through LDS, forms the score tile on
+// chip with bf16 MFMA (fp32 accumulation), keeps the running max m and sum l
+// per query in registers, rescales the output accumulator only when some
+// row's max changed, and divides by l once at the end, saving LSE = m + log l.
 //
 // Orientation: each wave computes S^T = K Q^T so that MFMA accumulator
 // columns are queries: a lane owns one query, the row max and row sum are
@@ -14,213 +14,247 @@
 // per-query rescale of O^T = V^T P^T is lane-local too. P^T leaves the
 // accumulators already in the B-operand layout of the P V product; V^T comes
 // from LDS through transposed 16-bit reads.
+//
+// Overlap: two wavefronts per SIMD, so one wave's softmax (VALU) runs while
+// the other's products occupy the matrix core; K/V tiles arrive by direct
+// global->LDS loads into double buffers while the current tile is consumed,
+// with one barrier per tile.
 #include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 
-template <int D, int QW, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
+namespace {
+
+constexpr int kNW = 8;    // wavefronts per workgroup
+constexpr int kQW = 32;   // query rows per wavefront
+constexpr int kBR = kNW * kQW;
+constexpr int kBC = 64;   // keys per tile
+constexpr int kThreads = kNW * 64;
+
+// Direct global->LDS loads of one [64 x D] bf16 tile. Thread `tid` fills the
+// 16-byte LDS chunks n * kThreads + tid of the tile; the source chunk is chosen
+// so that LDS holds the XOR-swizzled layout. Rows past the end are read from
+// row N-1 (finite values that are masked, or multiplied by P = 0).
+template <int D, bool IS_V>
+__device__ __forceinline__ void load_tile_async(uint16_t* lds_tile, const uint16_t* head, int k0, int N,
+                                                int tid) {
+  constexpr int CH = D / 8;
+  const int w = tid >> 6;
+#pragma unroll
+  for (int n = 0; n < (kBC * CH) / kThreads; ++n) {
+    const int e = n * kThreads + tid;  // 16-byte chunk index inside the tile
+    const int r = e / CH, p = e % CH;
+    const int c = p ^ (IS_V ? swz_v<D>(r) : swz_k<D>(r));
+    const int row = min(k0 + r, N - 1);
+    const uint16_t* src = head + (size_t)row * D + c * 8;
+    uint16_t* dst = lds_tile + (n * kThreads + w * 64) * 8;  // wave-uniform; lane l lands at +16 l bytes
+    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_loads_and_sync() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+}  // namespace
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads, 1)
 fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
            const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og, float* __restrict__ LSEg,
            int BH, int N, int nqb, float scale_log2) {
-  constexpr int NW = 4;            // wavefronts per workgroup
-  constexpr int BR = NW * QW;      // query rows per workgroup
-  constexpr int BC = 64;           // keys per tile
-  constexpr int QB = QW / 32;      // 32-query MFMA blocks per wave
-  constexpr int KS = D / 16;       // k-steps of the S product
-  constexpr int DB = D / 32;       // 32-row d blocks of O^T
-  constexpr int CH = D / 8;        // 16-byte chunks per row
+  constexpr int KS = D / 16;        // k-steps of the S product
+  constexpr int DB = D / 32;        // 32-row d blocks of O^T
+  constexpr int TILE = kBC * D;     // elements of one K or V tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BC * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BC * D];
+  // Four separate arrays so that the compiler can tell the buffer being filled
+  // by the direct loads from the one being read.
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int g = lane >> 4, i16 = lane & 15;
 
-  // Heaviest Q-blocks first (they have the most causal tiles).
-  const int qblk = nqb - 1 - (int)(blockIdx.x / BH);
-  const int bh = (int)(blockIdx.x % BH);
+  // Work id: one head's Q-blocks run together on one XCD (blocks are dispatched
+  // round-robin over the 8 XCDs) so its K/V stay in that XCD's L2; inside a
+  // head, the heaviest causal Q-blocks go first.
+  const int total = nqb * BH;
+  int wid = (int)blockIdx.x;
+  if ((total & 7) == 0) wid = (wid & 7) * (total >> 3) + (wid >> 3);
+  const int bh = wid / nqb;
+  const int qblk = CAUSAL ? nqb - 1 - (wid % nqb) : (wid % nqb);
   const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = Qg + head;
   const uint16_t* Kh = Kg + head;
   const uint16_t* Vh = Vg + head;
-  const int qw0 = qblk * BR + w * QW;  // first query row of this wave
+  const int qw0 = qblk * kBR + w * kQW;  // first query row of this wave
+  const int qrow = qw0 + l32;            // this lane's query
+
+  const int kend = CAUSAL ? min(N, qblk * kBR + kBR) : N;
+  const int ntiles = (kend + kBC - 1) / kBC;
+  // last tile this wave needs (causal: the one holding its diagonal)
+  const int wlast = CAUSAL ? min(ntiles - 1, (qw0 + kQW - 1) / kBC) : ntiles - 1;
+
+  load_tile_async<D, false>(sK0, Kh, 0, N, tid);
+  load_tile_async<D, true>(sV0, Vh, 0, N, tid);
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[q][16 ks + 8 hi .. +7].
-  bf16x8 qf[QB][KS];
+  bf16x8 qf[KS];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + qb * 32 + l32;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 u = {0, 0, 0, 0};
-      if (row < N) u = *(const u32x4*)(Qh + (size_t)row * D + ks * 16 + hi * 8);
-      qf[qb][ks] = as_bf16x8(u);
-    }
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 u = {0, 0, 0, 0};
+    if (qrow < N) u = *(const u32x4*)(Qg + head + (size_t)qrow * D + ks * 16 + hi * 8);
+    qf[ks] = as_bf16x8(u);
   }
 
-  f32x16 acc[QB][DB];
+  f32x16 acc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
-  float m[QB], l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
 
-  const int kend = CAUSAL ? min(N, qblk * BR + BR) : N;
-  const int ntiles = (kend + BC - 1) / BC;
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * BC;
-    __syncthreads();  // every wave is done with the previous tile
-#pragma unroll
-    for (int n = 0; n < (BC * CH) / 256; ++n) {
-      const int u = tid + 256 * n;
-      const int r = u / CH, c = u % CH;
-      const int key = k0 + r;
-      u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (key < N) {
-        kv = *(const u32x4*)(Kh + (size_t)key * D + c * 8);
-        vv = *(const u32x4*)(Vh + (size_t)key * D + c * 8);
-      }
-      *(u32x4*)(sK + r * D + ((c ^ swz_k<D>(r)) * 8)) = kv;
-      *(u32x4*)(sV + r * D + ((c ^ swz_v<D>(r)) * 8)) = vv;
+  // One tile: K(t), V(t) are in (sK, sV); the loads of tile t+1 go to (nK, nV).
+  auto tile = [&](int t, const uint16_t* sK, const uint16_t* sV, uint16_t* nK, uint16_t* nV) {
+    wait_loads_and_sync();  // tile t landed; every wave finished tile t-1
+    if (t + 1 < ntiles) {
+      load_tile_async<D, false>(nK, Kh, (t + 1) * kBC, N, tid);
+      load_tile_async<D, true>(nV, Vh, (t + 1) * kBC, N, tid);
     }
-    __syncthreads();
+    if (t > wlast) return;  // this wave's rows see none of these keys
+    const int k0 = t * kBC;
 
-    // Tiles entirely above the diagonal for this wave's rows: nothing to add.
-    if (CAUSAL && k0 > qw0 + QW - 1) continue;
-
-    // ---- S^T = K Q^T (two 32-key blocks x QB query blocks)
-    f32x16 s[2][QB];
+    // ---- S^T = K Q^T: two 32-key blocks (K operands read one k-step ahead)
+    f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    bf16x8 a[2], an[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+    for (int kb = 0; kb < 2; ++kb) {
+      const int r = kb * 32 + l32;
+      a[kb] = as_bf16x8(*(const u32x4*)(sK + r * D + ((hi ^ swz_k<D>(r)) * 8)));
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int r = kb * 32 + l32;
-        const int c = ks * 2 + hi;
-        const bf16x8 a = as_bf16x8(*(const u32x4*)(sK + r * D + ((c ^ swz_k<D>(r)) * 8)));
+        for (int kb = 0; kb < 2; ++kb) {
+          const int r = kb * 32 + l32;
+          const int c = (ks + 1) * 2 + hi;
+          an[kb] = as_bf16x8(*(const u32x4*)(sK + r * D + ((c ^ swz_k<D>(r)) * 8)));
+        }
+      }
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_bf16_32x32x16(a, qf[qb][ks], s[kb][qb]);
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_bf16_32x32x16(a[kb], qf[ks], s[kb]);
+      if (ks + 1 < KS) {
+        a[0] = an[0];
+        a[1] = an[1];
       }
     }
-
-    // ---- online softmax per query (lane-local plus one half-wave exchange)
-    u32x4 pb[2][2][QB];  // [kb][16-key step within kb][qb]: bf16x8 B operands of P V
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qrow = qw0 + qb * 32 + l32;
-      const bool need_mask = (CAUSAL && k0 + BC - 1 > qw0 + qb * 32) || (k0 + BC > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
-            const bool masked = (CAUSAL && key > qrow) || key >= N;
-            if (masked) s[kb][qb][i] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
+    // ---- online softmax (lane-local plus one half-wave exchange)
+    if ((CAUSAL && k0 + kBC - 1 > qw0) || (k0 + kBC > N)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-      mx = fmaxf(mx, other_half(mx));
-      const float m_new = fmaxf(m[qb], mx * scale_log2);
-      // m_new is finite: key 0 is visible to every row and sits in tile 0.
-      if (__any(m_new > m[qb])) {
-        const float alpha = fast_exp2(m[qb] - m_new);
-        l[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
-      }
-      m[qb] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          float p[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(__builtin_fmaf(s[kb][qb][8 * h2 + j], scale_log2, -m_new));
-            rs += p[j];
-          }
-          pb[kb][h2][qb] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
+          if ((CAUSAL && key > qrow) || key >= N) s[kb][i] = -INFINITY;
         }
-      }
-      l[qb] += rs;
     }
-
-    // ---- O^T += V^T P^T over four 16-key steps
-    const int g = lane >> 4, i16 = lane & 15;
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = (kb == 0 ? 2 : 0); i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
+    mx = fmaxf(mx, other_half(mx));
+    // finite: key 0 is visible to every row and sits in tile 0
+    const float m_new = fmaxf(m, mx * scale_log2);
+    if (__any(m_new > m)) {
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+    m = m_new;
+    float rs = 0.f;
+    u32x4 pb[2][2];  // [kb][16-key step]: bf16x8 B operands of P V
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = fast_exp2(__builtin_fmaf(s[kb][8 * h2 + j], scale_log2, -m_new));
+          rs += p[j];
+        }
+        pb[kb][h2] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+      }
+    }
+    l += rs;
+
+    // ---- O^T += V^T P^T over four 16-key steps
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int r0 = kb * 32 + 16 * h2 + 4 * hi + (i16 >> 2);
+        const int r1 = r0 + 8;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int d = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
           const int c = d >> 3, within = d & 7;
-          const int r0 = kb * 32 + 16 * h2 + 4 * hi + (i16 >> 2);
-          const int r1 = r0 + 8;
           const i16x4 t0 = lds_read_tr16(sV + r0 * D + ((c ^ swz_v<D>(r0)) * 8) + within);
           const i16x4 t1 = lds_read_tr16(sV + r1 * D + ((c ^ swz_v<D>(r1)) * 8) + within);
           const u32x4 au = {__builtin_bit_cast(u32x2, t0)[0], __builtin_bit_cast(u32x2, t0)[1],
                             __builtin_bit_cast(u32x2, t1)[0], __builtin_bit_cast(u32x2, t1)[1]};
-          const bf16x8 a = as_bf16x8(au);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            acc[qb][db] = mfma_bf16_32x32x16(a, as_bf16x8(pb[kb][h2][qb]), acc[qb][db]);
+          acc[db] = mfma_bf16_32x32x16(as_bf16x8(au), as_bf16x8(pb[kb][h2]), acc[db]);
         }
       }
     }
+  };
+
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    tile(t, sK0, sV0, sK1, sV1);
+    tile(t + 1, sK1, sV1, sK0, sV0);
   }
+  if (t < ntiles) tile(t, sK0, sV0, sK1, sV1);
 
   // ---- epilogue: divide once by l, store O (bf16) and LSE (natural log)
+  const float lt = l + other_half(l);
+  const float inv = 1.0f / lt;
+  if (qrow < N) {
+    uint16_t* orow = Og + head + (size_t)qrow * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l[qb] + other_half(l[qb]);
-    const float inv = 1.0f / lt;
-    const int row = qw0 + qb * 32 + l32;
-    if (row < N) {
-      uint16_t* orow = Og + head + (size_t)row * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d = db * 32 + 8 * g4 + 4 * hi;
-          const u32x2 pk = {pack_bf16x2(acc[qb][db][4 * g4 + 0] * inv, acc[qb][db][4 * g4 + 1] * inv),
-                            pack_bf16x2(acc[qb][db][4 * g4 + 2] * inv, acc[qb][db][4 * g4 + 3] * inv)};
-          *(u32x2*)(orow + d) = pk;
-        }
-      if (hi == 0) LSEg[(size_t)bh * N + row] = (m[qb] + __log2f(lt)) * kLn2;
-    }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * hi;
+        const u32x2 pk = {pack_bf16x2(acc[db][4 * g4 + 0] * inv, acc[db][4 * g4 + 1] * inv),
+                          pack_bf16x2(acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv)};
+        *(u32x2*)(orow + d) = pk;
+      }
+    if (hi == 0) LSEg[(size_t)bh * N + qrow] = (m + __log2f(lt)) * kLn2;
   }
 }
 
-template <int D, int QW, bool CAUSAL>
+template <int D, bool CAUSAL>
 static int launch(const FwdArgs& a) {
-  constexpr int BR = 4 * QW;
-  const int nqb = (a.N + BR - 1) / BR;
+  const int nqb = (a.N + kBR - 1) / kBR;
   const int BH = a.B * a.H;
-  const dim3 grid((unsigned)(nqb * BH)), block(256);
-  hipLaunchKernelGGL((fwd_kernel<D, QW, CAUSAL>), grid, block, 0, (hipStream_t)a.stream,
+  const dim3 grid((unsigned)(nqb * BH)), block(kThreads);
+  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), grid, block, 0, (hipStream_t)a.stream,
                      a.q, a.k, a.v, a.o, a.lse, BH, a.N, nqb, a.scale * kLog2e);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
 int launch_fwd(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch<128, 64, true>(a) : launch<128, 64, false>(a);
-  return a.causal ? launch<64, 64, true>(a) : launch<64, 64, false>(a);
+  if (a.d == 128) return a.causal ? launch<128, true>(a) : launch<128, false>(a);
+  return a.causal ? launch<64, true>(a) : launch<64, false>(a);
 }
 
 }  // namespace fa

@@ -92,6 +92,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=12)
+    ap.add_argument("--only", default=None,
+                    help="time only this kernel (fa_fwd, fa_bwd, fa_quant_fp8, fa_fwd_fp8) or 'copy', "
+                         "a plain 256 MiB device copy used to calibrate rocprofv3 byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
@@ -155,6 +158,12 @@ def main():
     if have_f8:
         kernels.append(("fa_fwd_fp8", lambda: fa.fwd_fp8(q8, k8, v8, qs, ks, vs, causal=True),
                         fwd_flops(B, H, N, D), fwd_bytes(B, H, N, D, 1), PEAK_FP8))
+    if args.only == "copy":
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        kernels = [("copy 256 MiB", lambda: dst.copy_(src), 0.0, 2.0 * src.numel(), None)]
+    elif args.only is not None:
+        kernels = [k for k in kernels if k[0].startswith(args.only)]
     if not kernels:
         raise RuntimeError("no kernel of the path is available")
 

@@ -25,6 +25,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no NaN inputs are assumed (NaN propagation is outside the contract), which
+    # lets fmaxf compile to a single v_max without operand canonicalisation
+    "-fno-honor-nans",
     "-I" + os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function",
 ]
 

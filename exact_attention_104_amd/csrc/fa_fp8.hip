@@ -11,13 +11,16 @@
 // strides 1, 2, 4 inside a lane's 8 values and 8, 16, 32, 64 across lanes;
 // then scale = fl32(amax / 448), codes = e4m3(clamp(fl32(x' * fl32(448 / amax)))).
 //
-// Forward: as the bf16 forward (split-Q waves of 64 query rows, S^T = K Q^T
-// so lanes own queries, online exp2 softmax with conditional rescale), on
+// Forward: as the bf16 forward (eight split-Q waves of 32 query rows, S^T =
+// K Q^T so lanes own queries, online exp2 softmax with conditional rescale,
+// direct global->LDS double-buffered tiles, one barrier per tile), on
 // v_mfma_f32_32x32x64 e4m3 products with fp32 accumulation. Block scales are
 // applied after the products: S = sq * sk * (Q8 K8^T). P is quantised to e4m3
 // for the P V product with the V block scale folded in: p' = p * sv_j * R with
 // R = 256 / max_j sv_j (so p' <= 256), the row sum keeps the unscaled p, and
 // the final division removes R.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -126,31 +129,71 @@ __device__ __forceinline__ int toff8(int row, int byte) {
   return row * D + ((((byte >> 4) ^ swz8<D>(row))) << 4) + (byte & 15);
 }
 
+namespace {
+
+constexpr int kF8NW = 8;              // wavefronts per workgroup
+constexpr int kF8QW = 32;             // query rows per wavefront
+constexpr int kF8BR = kF8NW * kF8QW;  // 256 query rows per workgroup
+constexpr int kF8BC = 64;             // keys per tile
+constexpr int kF8Threads = kF8NW * 64;
+
+// Direct global->LDS loads of one [64 x D] e4m3 tile into the swizzled layout
+// of toff8 (rows past the end read row N-1; they are masked or meet P = 0).
+template <int D>
+__device__ __forceinline__ void load_tile8_async(uint8_t* lds_tile, const uint8_t* head, int k0, int N, int tid) {
+  constexpr int CHB = D / 16;
+  constexpr int CHUNKS = kF8BC * CHB;  // 512 (D = 128) or 256 (D = 64)
+  if (CHUNKS < kF8Threads && tid >= CHUNKS) return;
+  const int w = tid >> 6;
+  const int r = tid / CHB, p = tid % CHB;
+  const int c = p ^ swz8<D>(r);
+  const int row = min(k0 + r, N - 1);
+  const uint8_t* src = head + (size_t)row * D + c * 16;
+  uint8_t* dst = lds_tile + w * 64 * 16;
+  __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+}
+
+}  // namespace
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(kF8Threads, 1)
 fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
                const float* __restrict__ QS, const float* __restrict__ KSc, const float* __restrict__ VS,
                uint16_t* __restrict__ Og, float* __restrict__ LSEg, int BH, int N, int nqb, int nsb,
                float scale_log2) {
-  constexpr int QW = 64, NW = 4, BR = NW * QW, BC = 64, QB = QW / 32;
   constexpr int KS = D / 64;      // k-steps of the S product (64 bytes each)
   constexpr int DB = D / 32;      // 32-row d blocks of O^T
-  constexpr int CHB = D / 16;     // 16-byte chunks per row
+  constexpr int TILE = kF8BC * D; // bytes of one K or V tile
 
-  __shared__ __attribute__((aligned(16))) uint8_t sK[BC * D];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[BC * D];
+  __shared__ __attribute__((aligned(16))) uint8_t sK0[TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t sK1[TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t sV0[TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t sV1[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   const int g = lane >> 4, i16 = lane & 15;
 
-  const int qblk = nqb - 1 - (int)(blockIdx.x / BH);
-  const int bh = (int)(blockIdx.x % BH);
+  const int total = nqb * BH;
+  int wid = (int)blockIdx.x;
+  if ((total & 7) == 0) wid = (wid & 7) * (total >> 3) + (wid >> 3);
+  const int bh = wid / nqb;
+  const int qblk = CAUSAL ? nqb - 1 - (wid % nqb) : (wid % nqb);
   const size_t head = (size_t)bh * (size_t)N * D;
-  const int qw0 = qblk * BR + w * QW;
+  const uint8_t* Kh = K8 + head;
+  const uint8_t* Vh = V8 + head;
+  const int qw0 = qblk * kF8BR + w * kF8QW;
+  const int qrow = qw0 + l32;
   const float* qs_h = QS + (size_t)bh * nsb;
   const float* ks_h = KSc + (size_t)bh * nsb;
   const float* vs_h = VS + (size_t)bh * nsb;
+
+  const int kend = CAUSAL ? min(N, qblk * kF8BR + kF8BR) : N;
+  const int ntiles = (kend + kF8BC - 1) / kF8BC;
+  const int wlast = CAUSAL ? min(ntiles - 1, (qw0 + kF8QW - 1) / kF8BC) : ntiles - 1;
+
+  load_tile8_async<D>(sK0, Kh, 0, N, tid);
+  load_tile8_async<D>(sV0, Vh, 0, N, tid);
 
   // R = 256 / max_j sv_j over the head, so every quantised p' = p sv_j R <= 256
   float svm = 0.f;
@@ -158,65 +201,40 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) svm = fmaxf(svm, __shfl_xor(svm, o));
   const float R = 256.f / svm;
-  const float sq = qs_h[min(qw0, N - 1) / 128];  // the wave's 64 rows share one scale block
+  const float sq = qs_h[min(qw0, N - 1) / 128];  // the wave's 32 rows share one scale block
 
   // Q8 as the B operand of S^T = K Q^T: lane holds Q8[q][64 ks + 32 hi .. +31]
-  i32x8 qf[QB][KS];
+  i32x8 qf[KS];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + qb * 32 + l32;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      i32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-      if (row < N) {
-        const uint8_t* p = Q8 + head + (size_t)row * D + ks * 64 + hi * 32;
-        a = *(const i32x4*)p;
-        b = *(const i32x4*)(p + 16);
-      }
-      qf[qb][ks] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  for (int ks = 0; ks < KS; ++ks) {
+    i32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+    if (qrow < N) {
+      const uint8_t* p = Q8 + head + (size_t)qrow * D + ks * 64 + hi * 32;
+      a = *(const i32x4*)p;
+      b = *(const i32x4*)(p + 16);
     }
+    qf[ks] = i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   }
 
-  f32x16 acc[QB][DB];
+  f32x16 acc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[qb][db] = f32x16{};
-  float m[QB], l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m[qb] = -INFINITY; l[qb] = 0.f; }
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
 
-  const int kend = CAUSAL ? min(N, qblk * BR + BR) : N;
-  const int ntiles = (kend + BC - 1) / BC;
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * BC;
+  auto tile = [&](int t, const uint8_t* sK, const uint8_t* sV, uint8_t* nK, uint8_t* nV,
+                  auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int k0 = t * kF8BC;
     const float sk = ks_h[k0 / 128], sv = vs_h[k0 / 128];
-    const float ct = sq * sk * scale_log2;  // exp2 domain scale of this tile's scores
+    const float ct = sq * sk * scale_log2;  // exp2-domain scale of this tile's scores
     const float ft = sv * R;                // factor folded into p' for the P V product
     const float tt = __log2f(ft);
     const float inv_ft = 1.f / ft;
-    __syncthreads();
-#pragma unroll
-    for (int n = 0; n < (BC * CHB) / 256; ++n) {
-      const int u = tid + 256 * n;
-      const int r = u / CHB, c = u % CHB;
-      i32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (k0 + r < N) {
-        kv = *(const i32x4*)(K8 + head + (size_t)(k0 + r) * D + c * 16);
-        vv = *(const i32x4*)(V8 + head + (size_t)(k0 + r) * D + c * 16);
-      }
-      *(i32x4*)(sK + toff8<D>(r, c * 16)) = kv;
-      *(i32x4*)(sV + toff8<D>(r, c * 16)) = vv;
-    }
-    __syncthreads();
-    if (CAUSAL && k0 > qw0 + QW - 1) continue;
 
     // ---- S^T = K8 Q8^T (fp32 accumulation; unscaled)
-    f32x16 s[2][QB];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+    f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
@@ -225,58 +243,52 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
         const i32x4 a0 = *(const i32x4*)(sK + toff8<D>(r, ks * 64 + hi * 32));
         const i32x4 a1 = *(const i32x4*)(sK + toff8<D>(r, ks * 64 + hi * 32 + 16));
         const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_fp8_32x32x64(a, qf[qb][ks], s[kb][qb]);
+        s[kb] = mfma_fp8_32x32x64(a, qf[ks], s[kb]);
       }
     }
 
     // ---- online softmax; p' = p * ft quantised to e4m3 (bytes in accumulator order)
-    i32x8 pb[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int qrow = qw0 + qb * 32 + l32;
-      const bool need_mask = (CAUSAL && k0 + BC - 1 > qw0 + qb * 32) || (k0 + BC > N);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
-            if ((CAUSAL && key > qrow) || key >= N) s[kb][qb][i] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
+    if constexpr (MASKED) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-      mx = fmaxf(mx, other_half(mx));
-      const float m_new = fmaxf(m[qb], mx * ct);
-      if (__any(m_new > m[qb])) {
-        const float alpha = fast_exp2(m[qb] - m_new);
-        l[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) acc[qb][db] *= alpha;
-      }
-      m[qb] = m_new;
-      const float off = tt - m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float p[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p[e] = fast_exp2(__builtin_fmaf(s[kb][qb][4 * q4 + e], ct, off));
-            rs += p[e];
-          }
-          pb[qb][kb * 4 + q4] = (int)pack_e4m3x4(fminf(p[0], 448.f), fminf(p[1], 448.f),
-                                                 fminf(p[2], 448.f), fminf(p[3], 448.f));
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
+          if ((CAUSAL && key > qrow) || key >= N) s[kb][i] = -INFINITY;
         }
-      }
-      l[qb] += rs * inv_ft;
     }
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = (kb == 0 ? 2 : 0); i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
+    mx = fmaxf(mx, other_half(mx));
+    const float m_new = fmaxf(m, mx * ct);
+    if (__any(m_new > m)) {
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+    }
+    m = m_new;
+    const float off = tt - m_new;
+    float rs = 0.f;
+    i32x8 pb;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = fast_exp2(__builtin_fmaf(s[kb][4 * q4 + e], ct, off));
+          rs += p[e];
+        }
+        pb[kb * 4 + q4] = (int)pack_e4m3x4(fminf(p[0], 448.f), fminf(p[1], 448.f), fminf(p[2], 448.f),
+                                           fminf(p[3], 448.f));
+      }
+    }
+    l += rs * inv_ft;
 
     // ---- O^T += V8^T P8^T: one 64-key MFMA per 32-row d block
 #pragma unroll
@@ -291,29 +303,61 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
         a[2 * rr] = t2[0];
         a[2 * rr + 1] = t2[1];
       }
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_fp8_32x32x64(a, pb[qb], acc[qb][db]);
+      acc[db] = mfma_fp8_32x32x64(a, pb, acc[db]);
     }
+  };
+
+  // One tile per step: wait for its loads, barrier, issue the next tile's
+  // loads, then compute. A tile needs the mask when it crosses the causal
+  // diagonal of the wave's rows or runs past N; without causality only the
+  // last tile can, so it is peeled off the unrolled loop.
+  auto step = [&](int t, const uint8_t* sK, const uint8_t* sV, uint8_t* nK, uint8_t* nV,
+                  auto last_tag) __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // tile t landed; every wave finished tile t-1
+    if (!LAST && t + 1 < ntiles) {
+      load_tile8_async<D>(nK, Kh, (t + 1) * kF8BC, N, tid);
+      load_tile8_async<D>(nV, Vh, (t + 1) * kF8BC, N, tid);
+    }
+    if (t > wlast) return;
+    const int k0 = t * kF8BC;
+    if constexpr (CAUSAL) {
+      if (k0 + kF8BC - 1 > qw0 || k0 + kF8BC > N)
+        tile(t, sK, sV, nK, nV, std::true_type{});
+      else
+        tile(t, sK, sV, nK, nV, std::false_type{});
+    } else {
+      tile(t, sK, sV, nK, nV, std::integral_constant<bool, LAST>{});
+    }
+  };
+
+  int t = 0;
+  for (; t + 2 < ntiles; t += 2) {
+    step(t, sK0, sV0, sK1, sV1, std::false_type{});
+    step(t + 1, sK1, sV1, sK0, sV0, std::false_type{});
+  }
+  if (t + 1 < ntiles) {
+    step(t, sK0, sV0, sK1, sV1, std::false_type{});
+    step(t + 1, sK1, sV1, sK0, sV0, std::true_type{});
+  } else {
+    step(t, sK0, sV0, sK1, sV1, std::true_type{});
   }
 
+  const float lt = l + other_half(l);
+  const float inv = 1.0f / (lt * R);
+  if (qrow < N) {
+    uint16_t* orow = Og + head + (size_t)qrow * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l[qb] + other_half(l[qb]);
-    const float inv = 1.0f / (lt * R);
-    const int row = qw0 + qb * 32 + l32;
-    if (row < N) {
-      uint16_t* orow = Og + head + (size_t)row * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d = db * 32 + 8 * g4 + 4 * hi;
-          const u32x2 pk = {pack_bf16x2(acc[qb][db][4 * g4 + 0] * inv, acc[qb][db][4 * g4 + 1] * inv),
-                            pack_bf16x2(acc[qb][db][4 * g4 + 2] * inv, acc[qb][db][4 * g4 + 3] * inv)};
-          *(u32x2*)(orow + d) = pk;
-        }
-      if (hi == 0) LSEg[(size_t)bh * N + row] = (m[qb] + __log2f(lt)) * kLn2;
-    }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * hi;
+        const u32x2 pk = {pack_bf16x2(acc[db][4 * g4 + 0] * inv, acc[db][4 * g4 + 1] * inv),
+                          pack_bf16x2(acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv)};
+        *(u32x2*)(orow + d) = pk;
+      }
+    if (hi == 0) LSEg[(size_t)bh * N + qrow] = (m + __log2f(lt)) * kLn2;
   }
 }
 
@@ -334,9 +378,9 @@ int launch_quant_fp8(const QuantArgs& a) {
 
 template <int D, bool CAUSAL>
 static int launch_f8(const Fp8FwdArgs& a) {
-  const int nqb = (a.N + 255) / 256, nsb = (a.N + 127) / 128;
+  const int nqb = (a.N + kF8BR - 1) / kF8BR, nsb = (a.N + 127) / 128;
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)(nqb * BH)), dim3(256), 0,
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)(nqb * BH)), dim3(kF8Threads), 0,
                      (hipStream_t)a.stream, a.q8, a.k8, a.v8, a.qs, a.ks, a.vs, a.o, a.lse, BH, a.N, nqb,
                      nsb, a.scale * kLog2e);
   return hipGetLastError() == hipSuccess ? 0 : 1;

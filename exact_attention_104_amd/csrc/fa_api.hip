@@ -99,7 +99,7 @@ int fa_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   if ((d != 64 && d != 128) || !shape_ok(B, H, N, d)) return 0;
-  return fa::bwd_dq_acc_bytes(B, H, N, d) + fa::bwd_delta_bytes(B, H, N);
+  return fa::bwd_delta_bytes(B, H, N);
 }
 
 int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
@@ -120,9 +120,7 @@ int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16
   const Range outs[4] = {span(dq, tb), span(dk, tb), span(dv, tb), span(ws, need)};
   if (any_alias(outs, 4, ins, 6)) return FA_ERR_ALIAS;
   if (int st = check_device()) return st;
-  float* dq_acc = (float*)ws;
-  float* delta = (float*)((char*)ws + fa::bwd_dq_acc_bytes(B, H, N, d));
-  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dq_acc, delta, B, H, N, d, causal, scale, stream};
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, (float*)ws, B, H, N, d, causal, scale, stream};
   return fa::launch_bwd(a) ? FA_ERR_LAUNCH : FA_OK;
 }
 

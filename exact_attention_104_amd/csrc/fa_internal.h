@@ -28,8 +28,7 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dq_acc;  // workspace: fp32 [B, H, N, d]
-  float* delta;   // workspace: fp32 [B, H, N]
+  float* delta;  // workspace: fp32 [B, H, N]
   int B, H, N, d, causal;
   float scale;
   void* stream;
@@ -64,11 +63,8 @@ int launch_bwd(const BwdArgs& a);
 int launch_quant_fp8(const QuantArgs& a);
 int launch_fwd_fp8(const Fp8FwdArgs& a);
 
-// Workspace layout of the backward pass (256-byte aligned pieces).
+// Workspace of the backward pass: D = rowsum(dO o O), rounded to 256 bytes.
 inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline size_t bwd_dq_acc_bytes(int B, int H, int N, int d) {
-  return round256((size_t)B * H * N * d * sizeof(float));
-}
 inline size_t bwd_delta_bytes(int B, int H, int N) { return round256((size_t)B * H * N * sizeof(float)); }
 
 }  // namespace fa

@@ -73,9 +73,9 @@ int fa_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
            int B, int H, int N, int d, int causal, float scale, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs: an fp32 dQ accumulator
- * [B, H, N, d] and the fp32 row vector D = rowsum(dO o O) [B, H, N], each
- * rounded up to 256 bytes. Returns 0 for invalid shapes.
+ * Bytes of device workspace fa_bwd needs: the fp32 row vector
+ * D = rowsum(dO o O) [B, H, N], rounded up to 256 bytes. Returns 0 for
+ * invalid shapes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
@@ -89,8 +89,8 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
  *   dq, dk, dv     : out, bf16 [B, H, N, d]
  *   ws, ws_bytes   : caller-owned device workspace, >= fa_bwd_workspace_bytes,
  *                    256-byte aligned; its contents on entry are ignored.
- * dK and dV are deterministic; dQ is accumulated with fp32 atomics and may
- * differ in the last bits between runs.
+ * No atomics: each output element is produced by one wave, so all three
+ * gradients are bitwise deterministic across runs.
  */
 int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
            const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,

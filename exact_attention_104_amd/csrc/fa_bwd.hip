@@ -72,8 +72,7 @@ __device__ __forceinline__ void load_tile_async(uint16_t* lds_tile, const uint16
     const int c = p ^ (TR ? swz2<D>(r) : swz_k<D>(r));
     const int row = min(r0 + r, N - 1);
     const uint16_t* src = head + (size_t)row * D + c * 8;
-    uint16_t* dst = lds_tile + (n * THREADS + w * 64) * 8;  // wave-uniform; lane l lands at +16 l bytes
-    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    lds_dma16(lds_tile + (n * THREADS + w * 64) * 8, src);  // lane l lands at +16 l bytes
   }
 }
 
@@ -82,11 +81,11 @@ __device__ __forceinline__ void load_ld_async(float* lds_ld, const float* lse_h,
                                               int lane) {
   const int r = min(q0 + (lane & 31), N - 1);
   const float* src = (lane < 32) ? lse_h + r : d_h + r;
-  __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)lds_ld, 4, 0, 0);
+  lds_dma4(lds_ld, src);
 }
 
 __device__ __forceinline__ void wait_loads_and_sync() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_vmem_all();
   __syncthreads();
 }
 

@@ -63,6 +63,33 @@ __device__ __forceinline__ float other_half(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Direct global->LDS loads (global_load_lds_dword[x4]): lane l's 4 or 16 bytes
+// from `src` land at lds_wave_base + size * l; lds_wave_base must be the same
+// for the whole wave. Issued through inline asm on purpose: the compiler then
+// does not track them, so it does not hold every LDS read of the other buffer
+// behind a wait for these loads (it cannot tell the buffers apart once the
+// buffer is chosen at run time). Every caller waits explicitly with
+// wait_vmem_all() and a barrier before reading what they wrote. M0 (the LDS
+// base operand) is saved and restored around the load.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void lds_dma16(void* lds_wave_base, const void* src) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(m0) : "memory");
+}
+__device__ __forceinline__ void lds_dma4(void* lds_wave_base, const void* src) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(m0) : "memory");
+}
+// vmcnt(0), other counters untouched: every vector memory operation of this
+// wave, including the loads above, has completed.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Two fp32 -> packed bf16 pair, round to nearest even.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};

@@ -149,8 +149,7 @@ __device__ __forceinline__ void load_tile8_async(uint8_t* lds_tile, const uint8_
   const int c = p ^ swz8<D>(r);
   const int row = min(k0 + r, N - 1);
   const uint8_t* src = head + (size_t)row * D + c * 16;
-  uint8_t* dst = lds_tile + w * 64 * 16;
-  __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  lds_dma16(lds_tile + w * 64 * 16, src);  // lane l lands at +16 l bytes
 }
 
 }  // namespace
@@ -314,7 +313,7 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   auto step = [&](int t, const uint8_t* sK, const uint8_t* sV, uint8_t* nK, uint8_t* nV,
                   auto last_tag) __attribute__((always_inline)) {
     constexpr bool LAST = decltype(last_tag)::value;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmem_all();
     __syncthreads();  // tile t landed; every wave finished tile t-1
     if (!LAST && t + 1 < ntiles) {
       load_tile8_async<D>(nK, Kh, (t + 1) * kF8BC, N, tid);

@@ -48,13 +48,12 @@ __device__ __forceinline__ void load_tile_async(uint16_t* lds_tile, const uint16
     const int c = p ^ (IS_V ? swz_v<D>(r) : swz_k<D>(r));
     const int row = min(k0 + r, N - 1);
     const uint16_t* src = head + (size_t)row * D + c * 8;
-    uint16_t* dst = lds_tile + (n * kThreads + w * 64) * 8;  // wave-uniform; lane l lands at +16 l bytes
-    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    lds_dma16(lds_tile + (n * kThreads + w * 64) * 8, src);  // lane l lands at +16 l bytes
   }
 }
 
 __device__ __forceinline__ void wait_loads_and_sync() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wait_vmem_all();
   __syncthreads();
 }
 

@@ -32,17 +32,9 @@ FLAGS = [
 ]
 
 
-# Per-file additions. fa_bwd.hip: the compiler's own MFMAs write VGPRs, so the
-# score accumulators that the VALU reads need no AGPR copies (the dK / dV
-# accumulators are pinned to AGPRs in the source).
-FILE_FLAGS = {
-    "fa_bwd.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
-}
-
-
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -1,0 +1,185 @@
+// dQ of the bf16 attention backward (third launch of fa_bwd; the method and
+// the first two launches are described in fa_bwd.hip).
+//
+// One workgroup per (batch, head, 256-row Q block): eight waves of 32 query
+// rows keep Q and dO (MFMA operands) and the dQ accumulator in registers and
+// stream 64-key K / V tiles: S^T = K Q^T and dP^T = V dO^T (lane = query),
+// P = exp2(S c - L log2 e) and dS = P o (dP - D) lane-locally, then
+// dQ^T += K^T dS^T with K read transposed ([HUB] "How it works": dQ = scale
+// dS K). Kept in its own file because it compiles best with MFMAs that write
+// VGPRs (the key-stationary kernel wants the opposite).
+#include <type_traits>
+
+#include "fa_bwd_tiles.h"
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kQNW = 8;    // dq: waves per workgroup
+constexpr int kQBR = kQNW * 32;  // dq: query rows per workgroup
+constexpr int kQBC = 64;   // dq: keys per tile
+constexpr int kQThreads = kQNW * 64;
+
+}  // namespace
+
+using namespace bwd;
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kQThreads, 1)
+dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
+          const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
+          uint16_t* __restrict__ dQg, int BH, int N, int nqb, float scale, float scale_log2) {
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TILE = kQBC * D;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int g = lane >> 4, i16 = lane & 15;
+
+  const int wid = xcd_work_id(nqb * BH);
+  const int bh = wid / nqb;
+  const int qblk = CAUSAL ? nqb - 1 - (wid % nqb) : (wid % nqb);
+  const size_t head = (size_t)bh * (size_t)N * D;
+  const uint16_t* Kh = Kg + head;
+  const uint16_t* Vh = Vg + head;
+  const int qw0 = qblk * kQBR + w * 32;
+  const int qrow = qw0 + l32;
+
+  const int kend = CAUSAL ? min(N, qblk * kQBR + kQBR) : N;
+  const int ntiles = (kend + kQBC - 1) / kQBC;
+  const int wlast = CAUSAL ? min(ntiles - 1, (qw0 + 31) / kQBC) : ntiles - 1;
+
+  load_tile_async<D, kQBC, kQThreads, true>(sK0, Kh, 0, N, tid);
+  load_tile_async<D, kQBC, kQThreads, true>(sV0, Vh, 0, N, tid);
+
+  // Q and dO as B operands of S^T = K Q^T and dP^T = V dO^T
+  bf16x8 qf[KS], of[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+    if (qrow < N) {
+      a = *(const u32x4*)(Qg + head + (size_t)qrow * D + ks * 16 + hi * 8);
+      b = *(const u32x4*)(dOg + head + (size_t)qrow * D + ks * 16 + hi * 8);
+    }
+    qf[ks] = as_bf16x8(a);
+    of[ks] = as_bf16x8(b);
+  }
+  // rows past N: L = +inf gives P = 0
+  const float Lq = qrow < N ? LSEg[(size_t)bh * N + qrow] * kLog2e : INFINITY;
+  const float Dq = qrow < N ? Dg[(size_t)bh * N + qrow] : 0.f;
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+
+  auto tile = [&](int t, const uint16_t* sK, const uint16_t* sV, auto masked_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int k0 = t * kQBC;
+    // The lane index passes through an empty asm so that the LDS addresses
+    // derived from it are formed inside the tile rather than hoisted out of
+    // the loop for both tile variants (which would not fit in registers).
+    int lp = lane;
+    asm volatile("" : "+v"(lp));
+    const int l32 = lp & 31, hi = lp >> 5, g = lp >> 4, i16 = lp & 15;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // ---- S^T and dP^T for 32 keys (lane = query)
+      const int r = kb * 32 + l32;
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int col = ks * 16 + hi * 8;
+        const bf16x8 ak = as_bf16x8(*(const u32x4*)(sK + toff<D>(r, col)));
+        const bf16x8 av = as_bf16x8(*(const u32x4*)(sV + toff<D>(r, col)));
+        s = mfma_bf16_32x32x16(ak, qf[ks], s);
+        dp = mfma_bf16_32x32x16(av, of[ks], dp);
+      }
+      // ---- dS^T = P^T o (dP^T - D), packed as the B operands of K^T dS^T
+      u32x4 dsb[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        float ds[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * h2 + j;
+          float pv = fast_exp2(__builtin_fmaf(s[i], scale_log2, -Lq));
+          if constexpr (MASKED) {
+            const int key = k0 + kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
+            if ((CAUSAL && key > qrow) || key >= N) pv = 0.f;
+          }
+          ds[j] = pv * (dp[i] - Dq);
+        }
+        dsb[h2] = u32x4{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
+                        pack_bf16x2(ds[6], ds[7])};
+      }
+      // ---- dQ^T += K^T dS^T over two 16-key steps (K read transposed)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int r0 = kb * 32 + 16 * h2 + 4 * hi + (i16 >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int d = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
+          const u32x4 au = tr_pair(sK + toff<D>(r0, d), sK + toff<D>(r0 + 8, d));
+          acc[db] = mfma_bf16_32x32x16(as_bf16x8(au), as_bf16x8(dsb[h2]), acc[db]);
+        }
+      }
+    }
+  };
+
+  // Buffers alternate by tile parity (not unrolled, for the same reason).
+  for (int t = 0; t < ntiles; ++t) {
+    const bool odd = t & 1;
+    wait_loads_and_sync();  // tile t landed; every wave finished tile t-1
+    if (t + 1 < ntiles) {
+      load_tile_async<D, kQBC, kQThreads, true>(odd ? sK0 : sK1, Kh, (t + 1) * kQBC, N, tid);
+      load_tile_async<D, kQBC, kQThreads, true>(odd ? sV0 : sV1, Vh, (t + 1) * kQBC, N, tid);
+    }
+    if (t > wlast) continue;  // this wave's rows see none of these keys
+    const int k0 = t * kQBC;
+    const uint16_t* sK = odd ? sK1 : sK0;
+    const uint16_t* sV = odd ? sV1 : sV0;
+    if ((CAUSAL && k0 + kQBC - 1 > qw0) || k0 + kQBC > N)
+      tile(t, sK, sV, std::true_type{});
+    else
+      tile(t, sK, sV, std::false_type{});
+  }
+
+  // ---- dQ = scale dQ^T^T, bf16 (lane = query, d over the accumulator rows)
+  if (qrow < N) {
+    uint16_t* row = dQg + head + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + 8 * g4 + 4 * hi;
+        const u32x2 pk = {pack_bf16x2(acc[db][4 * g4 + 0] * scale, acc[db][4 * g4 + 1] * scale),
+                          pack_bf16x2(acc[db][4 * g4 + 2] * scale, acc[db][4 * g4 + 3] * scale)};
+        *(u32x2*)(row + d) = pk;
+      }
+  }
+}
+
+template <int D, bool CAUSAL>
+static int launch_dq(const BwdArgs& a) {
+  const int BH = a.B * a.H;
+  const int nqb = (a.N + kQBR - 1) / kQBR;
+  hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb * BH)), dim3(kQThreads), 0, (hipStream_t)a.stream,
+                     a.q, a.k, a.v, a.dO, a.lse, a.delta, a.dq, BH, a.N, nqb, a.scale, a.scale * kLog2e);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+int launch_bwd_dq(const BwdArgs& a) {
+  if (a.d == 128) return a.causal ? launch_dq<128, true>(a) : launch_dq<128, false>(a);
+  return a.causal ? launch_dq<64, true>(a) : launch_dq<64, false>(a);
+}
+
+}  // namespace fa

@@ -58,6 +58,27 @@ def quant_bytes(b, h, n, d):
     return b * h * n * d * (2 + 1) + 4.0 * b * h * ((n + 127) // 128)
 
 
+def measured_traffic(path: str):
+    """Bytes per launch from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary,
+    or None when the kernel sources listed there changed since it was taken."""
+    import hashlib
+    try:
+        fields = {}
+        for line in open(path):
+            if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_launch", "source_sha1", "sources"):
+                k, v = line.split(":", 1)
+                fields[k] = v.strip()
+        h = hashlib.sha1()
+        for src in fields["sources"].split():
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != fields["source_sha1"]:
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(sample_heads: int):
     """The fp64 oracle (as it stands) on `sample_heads` heads of the bf16
     workload: one forward and one backward per head."""
@@ -93,8 +114,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=12)
     ap.add_argument("--only", default=None,
-                    help="time only this kernel (fa_fwd, fa_bwd, fa_quant_fp8, fa_fwd_fp8) or 'copy', "
-                         "a plain 256 MiB device copy used to calibrate rocprofv3 byte counters")
+                    help="time only this kernel (fa_fwd, fa_bwd, fa_quant_fp8, fa_fwd_fp8) or 'copy[MiB]', "
+                         "a plain device copy (default 256 MiB) used to calibrate rocprofv3 byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
@@ -158,10 +179,11 @@ def main():
     if have_f8:
         kernels.append(("fa_fwd_fp8", lambda: fa.fwd_fp8(q8, k8, v8, qs, ks, vs, causal=True),
                         fwd_flops(B, H, N, D), fwd_bytes(B, H, N, D, 1), PEAK_FP8))
-    if args.only == "copy":
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        kernels = [("copy 256 MiB", lambda: dst.copy_(src), 0.0, 2.0 * src.numel(), None)]
+    if args.only is not None and args.only.startswith("copy"):
+        mib = int(args.only[4:] or 256)
+        src = torch.full((mib << 20,), 7, dtype=torch.uint8, device=dev)  # written, so its reads are real
+        dst = torch.zeros_like(src)
+        kernels = [("copy %d MiB" % mib, lambda: dst.copy_(src), 0.0, 2.0 * src.numel(), None)]
     elif args.only is not None:
         kernels = [k for k in kernels if k[0].startswith(args.only)]
     if not kernels:
@@ -207,9 +229,13 @@ def main():
     name, flops, nbytes, peak = dom
     if peak:
         achieved = breakdown[name]["tflops"]
+        traffic = None
+        if name == "fa_bwd":  # one C-ABI launch: pre_kernel, dkdv_kernel, dq_kernel
+            traffic = measured_traffic(os.path.join(ROOT, "profiles", "fa_bwd_n8192_d128_causal_hbm_bytes.md"))
         roofline = {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": peak,
-                    "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
-                    "per_launch_flops": flops, "avg_launch_ms": breakdown[name]["ms_avg"]}
+                    "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
+                    "per_launch_flops": flops, "avg_launch_ms": breakdown[name]["ms_avg"],
+                    "algorithmic_bytes": nbytes}
     else:
         achieved = breakdown[name]["gbps"]
         roofline = {"kernel": name, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM,

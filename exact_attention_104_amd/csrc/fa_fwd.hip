@@ -6,7 +6,9 @@
 // (split-Q), streams 64-key K/V tiles through LDS, forms the score tile on
 // chip with bf16 MFMA (fp32 accumulation), keeps the running max m and sum l
 // per query in registers, rescales the output accumulator only when some
-// row's max changed, and divides by l once at the end, saving LSE = m + log l.
+// row's max grew by more than a fixed slack ([LIB] "FA4": skip the rescale
+// unless the max changes significantly; exact, since O and l share the same
+// stale max), and divides by l once at the end, saving LSE = m + log l.
 //
 // Orientation: each wave computes S^T = K Q^T so that MFMA accumulator
 // columns are queries: a lane owns one query, the row max and row sum are
@@ -31,6 +33,10 @@ constexpr int kQW = 32;   // query rows per wavefront
 constexpr int kBR = kNW * kQW;
 constexpr int kBC = 64;   // keys per tile
 constexpr int kThreads = kNW * 64;
+#ifndef FA_RESCALE_SLACK
+#define FA_RESCALE_SLACK 8.0f
+#endif
+constexpr float kRescaleSlack = FA_RESCALE_SLACK;  // log2 units; P stays <= 256 in bf16
 
 // Direct global->LDS loads of one [64 x D] bf16 tile. Thread `tid` fills the
 // 16-byte LDS chunks n * kThreads + tid of the tile; the source chunk is chosen
@@ -167,16 +173,19 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = (kb == 0 ? 2 : 0); i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
-    mx = fmaxf(mx, other_half(mx));
-    // finite: key 0 is visible to every row and sits in tile 0
-    const float m_new = fmaxf(m, mx * scale_log2);
-    if (__any(m_new > m)) {
+    mx = fmaxf(mx, other_half(mx)) * scale_log2;
+    // finite: key 0 is visible to every row and sits in tile 0. The running
+    // max is replaced (and O, l rescaled) only when some row's max exceeds it
+    // by more than kRescaleSlack: until then p <= 2^kRescaleSlack, and O and l
+    // share the same stale max, so O / l and the LSE are unchanged.
+    if (__any(mx > m + kRescaleSlack)) {
+      const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      m = m_new;
     }
-    m = m_new;
     float rs = 0.f;
     u32x4 pb[2][2];  // [kb][16-key step]: bf16x8 B operands of P V
 #pragma unroll
@@ -186,7 +195,7 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          p[j] = fast_exp2(__builtin_fmaf(s[kb][8 * h2 + j], scale_log2, -m_new));
+          p[j] = fast_exp2(__builtin_fmaf(s[kb][8 * h2 + j], scale_log2, -m));
           rs += p[j];
         }
         pb[kb][h2] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),

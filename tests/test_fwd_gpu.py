@@ -90,3 +90,20 @@ def test_fwd_scale_argument(gpu):
     torch.cuda.synchronize()
     o_ref, lse_ref = A.forward(host["q"], host["k"], host["v"], False, 0.37)
     _check(to_host(o), to_host(lse), o_ref, lse_ref, "scale 0.37")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_late_max_jump(gpu, causal):
+    """Keys far past the first tiles (rows 600..615) scaled by 8 (exact in bf16) raise
+    the rows' score maxima by far more than the kernel's rescale slack after several
+    tiles, so the delayed rescale of O and l runs mid-sequence."""
+    from gpu_util import to_dev
+    import fa_inputs
+    B, H, N, d = 1, 2, 1000, 128
+    host = fa_inputs.attention_inputs(B, H, N, d, 31)
+    host["k"][:, :, 600:616, :] *= 8.0
+    dev = {k: to_dev(v) for k, v in host.items()}
+    o, lse = gpu.fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = A.forward(host["q"], host["k"], host["v"], causal, 1.0 / math.sqrt(d))
+    _check(to_host(o), to_host(lse), o_ref, lse_ref, "late max jump c%d" % causal)

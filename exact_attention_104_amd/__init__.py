@@ -7,6 +7,8 @@ raises.
 
     o, lse = fwd(q, k, v, causal=True)                  # bf16 [B, H, N, d] CUDA tensors
     dq, dk, dv = bwd(q, k, v, o, do, lse, causal=True)
+    # any [B, H, N, d] views with contiguous d (e.g. [B, N, H, d].transpose(1, 2)),
+    # and grouped K/V heads: k, v of shape [B, H_kv, N, d] with H_kv dividing H
     q8, qs = quant_fp8(q, signs)                        # signs: int8 [128] or None
     o8, lse8 = fwd_fp8(q8, k8, v8, qs, ks, vs, causal=True)
 """
@@ -32,13 +34,20 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
 
+class Strides(ctypes.Structure):
+    """fa_strides: element strides (batch, head, row) of a [B, H, N, d] view."""
+    _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("row", ctypes.c_int64)]
+
+
 # exported symbol -> (restype, argtypes)
 SIGNATURES = {
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_abi_version": (_I, []),
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "fa_fwd_strided": (_I, [_P] * 5 + [_I, _I, _I, _I, _I, _P, _I, _F, _P]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _F, _P, ctypes.c_size_t, _P]),
+    "fa_bwd_strided": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _P, _I, _F, _P, ctypes.c_size_t, _P]),
     "fa_quant_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_fwd_fp8": (_I, [_P] * 8 + [_I, _I, _I, _I, _I, _F, _P]),
 }
@@ -99,6 +108,35 @@ def _bhnd(q):
     return tuple(int(x) for x in q.shape)
 
 
+def _check_view(name, t, shape):
+    """A bf16 [B, H, N, d] view on the GPU whose last dimension is contiguous."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.bfloat16:
+        raise TypeError("%s must be torch.bfloat16, got %s" % (name, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be on a GPU" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.stride(3) != 1:
+        raise ValueError("%s must have a contiguous last dimension" % name)
+
+
+def _strides(*ts):
+    arr = (Strides * len(ts))()
+    for i, t in enumerate(ts):
+        arr[i] = Strides(t.stride(0), t.stride(1), t.stride(2))
+    return arr
+
+
+def _kv_heads(q, k, v):
+    B, H, N, d = _bhnd(q)
+    Hkv = int(k.shape[1]) if k.dim() == 4 else -1
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("k, v need H_kv heads with H_kv dividing H = %d, got %s" % (H, tuple(k.shape)))
+    return B, H, Hkv, N, d
+
+
 def _scale(scale, d):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
@@ -109,18 +147,28 @@ def _raise(st, call):
 
 
 def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """bf16 forward: returns (O bf16 [B,H,N,d], LSE fp32 [B,H,N])."""
+    """bf16 forward: returns (O bf16 [B,H,N,d], LSE fp32 [B,H,N]).
+
+    q: [B, H, N, d]; k, v: [B, H_kv, N, d] (H_kv divides H: grouped / multi-query
+    heads); any views with a contiguous last dimension. O takes q's layout."""
     lib = load_library()
-    B, H, N, d = _bhnd(q)
-    for n, t in (("q", q), ("k", k), ("v", v)):
-        _check_tensor(n, t, torch.bfloat16, (B, H, N, d))
+    B, H, Hkv, N, d = _kv_heads(q, k, v)
+    _check_view("q", q, (B, H, N, d))
+    _check_view("k", k, (B, Hkv, N, d))
+    _check_view("v", v, (B, Hkv, N, d))
     o = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check_tensor("out", o, torch.bfloat16, (B, H, N, d))
+    _check_view("out", o, (B, H, N, d))
     _check_tensor("lse", lse_t, torch.float32, (B, H, N))
-    st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
-                    B, H, N, d, int(bool(causal)), _scale(scale, d), _stream())
-    _raise(st, "fa_fwd")
+    sc, c = _scale(scale, d), int(bool(causal))
+    if Hkv == H and all(t.is_contiguous() for t in (q, k, v, o)):
+        st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
+                        B, H, N, d, c, sc, _stream())
+        _raise(st, "fa_fwd")
+    else:
+        st = lib.fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
+                                B, H, Hkv, N, d, _strides(q, k, v, o), c, sc, _stream())
+        _raise(st, "fa_fwd_strided")
     return o, lse_t
 
 
@@ -129,21 +177,31 @@ def bwd_workspace_bytes(B, H, N, d) -> int:
 
 
 def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, workspace=None):
-    """bf16 backward by recomputation: returns (dQ, dK, dV) bf16 [B,H,N,d]."""
+    """bf16 backward by recomputation: returns (dQ, dK, dV) bf16.
+
+    Shapes and layouts as in fwd; dK, dV have k's and v's shapes and layouts
+    (for grouped heads, the sums over each group's query heads)."""
     lib = load_library()
-    B, H, N, d = _bhnd(q)
-    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
-        _check_tensor(n, t, torch.bfloat16, (B, H, N, d))
+    B, H, Hkv, N, d = _kv_heads(q, k, v)
+    for n, t in (("q", q), ("o", o), ("do", do)):
+        _check_view(n, t, (B, H, N, d))
+    for n, t in (("k", k), ("v", v)):
+        _check_view(n, t, (B, Hkv, N, d))
     _check_tensor("lse", lse, torch.float32, (B, H, N))
     need = bwd_workspace_bytes(B, H, N, d)
     ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
     _check_tensor("workspace", ws, torch.uint8)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                    B, H, N, d, int(bool(causal)), _scale(scale, d), ws.data_ptr(), ws.numel(),
-                    _stream())
-    _raise(st, "fa_bwd")
+    sc, c = _scale(scale, d), int(bool(causal))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    if Hkv == H and all(t.is_contiguous() for t in (q, k, v, o, do, dq, dk, dv)):
+        st = lib.fa_bwd(*ptrs, B, H, N, d, c, sc, ws.data_ptr(), ws.numel(), _stream())
+        _raise(st, "fa_bwd")
+    else:
+        st = lib.fa_bwd_strided(*ptrs, B, H, Hkv, N, d, _strides(q, k, v, o, do, dq, dk, dv), c, sc,
+                                ws.data_ptr(), ws.numel(), _stream())
+        _raise(st, "fa_bwd_strided")
     return dq, dk, dv
 
 

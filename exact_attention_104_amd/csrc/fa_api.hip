@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <utility>
 
 #include "../../include/fa.h"
 #include "fa_internal.h"
@@ -58,6 +59,43 @@ bool scalars_ok(int causal, float scale) {
   return (causal == 0 || causal == 1) && std::isfinite(scale) && scale > 0.f;
 }
 
+// A [B, Hx, N, d] view with element strides st and contiguous d.
+struct View {
+  const void* p;
+  long long B, H, N, d;
+  fa_strides st;
+  // bytes from p to one past the last element
+  size_t bytes() const {
+    return 2u * (size_t)((B - 1) * st.batch + (H - 1) * st.head + (N - 1) * st.row + d);
+  }
+  Range range() const { return span(p, bytes()); }
+  // rows start on 16-byte boundaries (the kernels load 16-byte chunks)
+  bool aligned() const {
+    return aligned16(p) && st.batch % 8 == 0 && st.head % 8 == 0 && st.row % 8 == 0;
+  }
+  // row strides stay below 2^31 elements: the kernels form row offsets with
+  // one 32 x 32 -> 64-bit multiply
+  bool strides_ok() const { return st.batch > 0 && st.head > 0 && st.row > 0 && st.row <= 0x7fffffffLL; }
+  // no two elements share an address: with dims of extent > 1 sorted by stride,
+  // each stride exceeds the span of all finer dims (d counts as stride 1)
+  bool injective() const {
+    long long ext[3] = {B, H, N}, str[3] = {st.batch, st.head, st.row};
+    for (int i = 0; i < 3; ++i)
+      for (int j = i + 1; j < 3; ++j)
+        if (str[j] < str[i]) {
+          std::swap(str[i], str[j]);
+          std::swap(ext[i], ext[j]);
+        }
+    long long reach = d;  // elements spanned by the finer dims
+    for (int i = 0; i < 3; ++i) {
+      if (ext[i] == 1) continue;
+      if (str[i] < reach) return false;
+      reach = str[i] * (ext[i] - 1) + reach;
+    }
+    return true;
+  }
+};
+
 }  // namespace
 
 extern "C" {
@@ -80,21 +118,34 @@ const char* fa_status_string(int status) {
 
 int fa_abi_version(void) { return FA_ABI_VERSION; }
 
+int fa_fwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                   int B, int H, int H_kv, int N, int d, const fa_strides* st, int causal, float scale,
+                   void* stream) {
+  if (!scalars_ok(causal, scale)) return FA_ERR_ARG;
+  if (!q || !k || !v || !o || !lse || !st) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!shape_ok(B, H, N, d) || H_kv < 1 || H % H_kv != 0) return FA_ERR_SHAPE;
+  const View vq{q, B, H, N, d, st[0]}, vk{k, B, H_kv, N, d, st[1]}, vv{v, B, H_kv, N, d, st[2]},
+      vo{o, B, H, N, d, st[3]};
+  if (!vq.strides_ok() || !vk.strides_ok() || !vv.strides_ok() || !vo.strides_ok()) return FA_ERR_ARG;
+  if (!vq.aligned() || !vk.aligned() || !vv.aligned() || !vo.aligned() || !aligned16(lse)) return FA_ERR_ALIGN;
+  const size_t lb = (size_t)B * H * N * 4;
+  const Range ins[3] = {vq.range(), vk.range(), vv.range()};
+  const Range outs[2] = {vo.range(), span(lse, lb)};
+  if (!vo.injective() || any_alias(outs, 2, ins, 3)) return FA_ERR_ALIAS;
+  if (int s = check_device()) return s;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N, d, causal, scale,
+                fa::Strides{st[0].batch, st[0].head, st[0].row}, fa::Strides{st[1].batch, st[1].head, st[1].row},
+                fa::Strides{st[2].batch, st[2].head, st[2].row}, fa::Strides{st[3].batch, st[3].head, st[3].row},
+                stream};
+  return fa::launch_fwd(a) ? FA_ERR_LAUNCH : FA_OK;
+}
+
 int fa_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
            int B, int H, int N, int d, int causal, float scale, void* stream) {
-  if (!scalars_ok(causal, scale)) return FA_ERR_ARG;
-  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (!shape_ok(B, H, N, d)) return FA_ERR_SHAPE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-    return FA_ERR_ALIGN;
-  const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
-  const Range ins[3] = {span(q, tb), span(k, tb), span(v, tb)};
-  const Range outs[2] = {span(o, tb), span(lse, lb)};
-  if (any_alias(outs, 2, ins, 3)) return FA_ERR_ALIAS;
-  if (int st = check_device()) return st;
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, causal, scale, stream};
-  return fa::launch_fwd(a) ? FA_ERR_LAUNCH : FA_OK;
+  const fa_strides c{(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
+  const fa_strides st[4] = {c, c, c, c};
+  return fa_fwd_strided(q, k, v, o, lse, B, H, H, N, d, st, causal, scale, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -102,26 +153,43 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   return fa::bwd_delta_bytes(B, H, N);
 }
 
+int fa_bwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                   const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                   int B, int H, int H_kv, int N, int d, const fa_strides* st, int causal, float scale,
+                   void* ws, size_t ws_bytes, void* stream) {
+  if (!scalars_ok(causal, scale)) return FA_ERR_ARG;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !st) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!shape_ok(B, H, N, d) || H_kv < 1 || H % H_kv != 0) return FA_ERR_SHAPE;
+  const View vq{q, B, H, N, d, st[0]}, vk{k, B, H_kv, N, d, st[1]}, vv{v, B, H_kv, N, d, st[2]},
+      vo{o, B, H, N, d, st[3]}, vdo{dO, B, H, N, d, st[4]}, vdq{dq, B, H, N, d, st[5]},
+      vdk{dk, B, H_kv, N, d, st[6]}, vdv{dv, B, H_kv, N, d, st[7]};
+  const View* all[8] = {&vq, &vk, &vv, &vo, &vdo, &vdq, &vdk, &vdv};
+  for (const View* x : all)
+    if (!x->strides_ok()) return FA_ERR_ARG;
+  for (const View* x : all)
+    if (!x->aligned()) return FA_ERR_ALIGN;
+  if (!aligned16(lse)) return FA_ERR_ALIGN;
+  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+  if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t lb = (size_t)B * H * N * 4;
+  const Range ins[6] = {vq.range(), vk.range(), vv.range(), vo.range(), vdo.range(), span(lse, lb)};
+  const Range outs[4] = {vdq.range(), vdk.range(), vdv.range(), span(ws, need)};
+  if (!vdq.injective() || !vdk.injective() || !vdv.injective() || any_alias(outs, 4, ins, 6)) return FA_ERR_ALIAS;
+  if (int s = check_device()) return s;
+  auto S = [&](int i) { return fa::Strides{st[i].batch, st[i].head, st[i].row}; };
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, (float*)ws, B, H, H_kv, N, d, causal, scale,
+                S(0), S(1), S(2), S(3), S(4), S(5), S(6), S(7), stream};
+  return fa::launch_bwd(a) ? FA_ERR_LAUNCH : FA_OK;
+}
+
 int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
            const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
            int B, int H, int N, int d, int causal, float scale, void* ws, size_t ws_bytes,
            void* stream) {
-  if (!scalars_ok(causal, scale)) return FA_ERR_ARG;
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (!shape_ok(B, H, N, d)) return FA_ERR_SHAPE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) ||
-      !aligned16(lse) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return FA_ERR_ALIGN;
-  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
-  if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need) return FA_ERR_WORKSPACE;
-  const size_t tb = (size_t)B * H * N * d * 2, lb = (size_t)B * H * N * 4;
-  const Range ins[6] = {span(q, tb), span(k, tb), span(v, tb), span(o, tb), span(dO, tb), span(lse, lb)};
-  const Range outs[4] = {span(dq, tb), span(dk, tb), span(dv, tb), span(ws, need)};
-  if (any_alias(outs, 4, ins, 6)) return FA_ERR_ALIAS;
-  if (int st = check_device()) return st;
-  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, (float*)ws, B, H, N, d, causal, scale, stream};
-  return fa::launch_bwd(a) ? FA_ERR_LAUNCH : FA_OK;
+  const fa_strides c{(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
+  const fa_strides st[8] = {c, c, c, c, c, c, c, c};
+  return fa_bwd_strided(q, k, v, o, dO, lse, dq, dk, dv, B, H, H, N, d, st, causal, scale, ws, ws_bytes, stream);
 }
 
 int fa_quant_fp8(const uint16_t* x, uint8_t* x8, float* scales, const int8_t* signs_or_null,

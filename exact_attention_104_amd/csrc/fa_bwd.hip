@@ -45,18 +45,19 @@ using namespace bwd;
 template <int D>
 __global__ void __launch_bounds__(256)
 pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, float* __restrict__ delta,
-           long long rows) {
+           long long rows, int H, int N, Strides so, Strides sdo) {
   constexpr int LPR = D / 8;        // lanes per row, 8 elements each
   constexpr int RPB = 256 / LPR;    // rows per block
   const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
   const int c = threadIdx.x % LPR;
   float s = 0.f;
   if (row < rows) {
-    const size_t off = (size_t)row * D + c * 8;
-    const u32x4 a = *(const u32x4*)(O + off);
-    const u32x4 b = *(const u32x4*)(dO + off);
+    const long long bh = row / N;
+    const int n = (int)(row % N), b = (int)(bh / H), h = (int)(bh % H);
+    const u32x4 a = *(const u32x4*)(O + b * so.b + h * so.h + (long long)n * so.n + c * 8);
+    const u32x4 e = *(const u32x4*)(dO + b * sdo.b + h * sdo.h + (long long)n * sdo.n + c * 8);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s += bf16_lo(a[j]) * bf16_lo(b[j]) + bf16_hi(a[j]) * bf16_hi(b[j]);
+    for (int j = 0; j < 4; ++j) s += bf16_lo(a[j]) * bf16_lo(e[j]) + bf16_hi(a[j]) * bf16_hi(e[j]);
   }
 #pragma unroll
   for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
@@ -70,8 +71,9 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1)
 dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
             const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
-            uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, int BH, int N, int nkb, float scale,
-            float scale_log2) {
+            uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, int BHkv, int H, int group, int N, int nkb,
+            float scale, float scale_log2, Strides sq, Strides sk, Strides sv, Strides sdo, Strides sdk,
+            Strides sdv) {
   constexpr int KS = D / 16;    // k-steps over d
   constexpr int DB = D / 32;    // 32-wide d blocks
   constexpr int QT = kBQ * D;   // elements of a Q or dO tile
@@ -91,40 +93,55 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
 
-  // One head's key blocks run together on one XCD, heaviest causal block first.
-  const int wid = xcd_work_id(nkb * BH);
-  const int bh = wid / nkb;
+  // One K/V head's key blocks run together on one XCD, heaviest causal block
+  // first. The block's keys serve the group query heads hk * group + g.
+  const int wid = xcd_work_id(nkb * BHkv);
+  const int bhk = wid / nkb;
   const int kblk = wid % nkb;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = Qg + head;
-  const uint16_t* dOh = dOg + head;
-  const float* lse_h = LSEg + (size_t)bh * N;
-  const float* d_h = Dg + (size_t)bh * N;
+  const int Hkv = H / group;
+  const int b = bhk / Hkv, hk = bhk % Hkv;
+  const uint16_t* Kh = Kg + b * sk.b + hk * sk.h;
+  const uint16_t* Vh = Vg + b * sv.b + hk * sv.h;
   const int kb0 = kblk * kBKC;
   const int kw0 = kb0 + w * 32;
   const int key_l = kw0 + (lane & 31);  // this lane's key in S / dP
 
-  // Step j handles query block nqs - 1 - j: from the last block down, so that
-  // the concurrent key blocks of a head read the same Q / dO tiles at about
-  // the same time. Causal: blocks below the key block are all masked.
+  // Steps run over the group's query heads hk * group + 0 .. group - 1 in
+  // turn; within a head, from the last query block down (so that the
+  // concurrent key blocks of a head read the same Q / dO tiles at about the
+  // same time) to block qs_lo (causal: blocks below the key block are all
+  // masked).
   const int nqs = (N + kBQ - 1) / kBQ;
   const int qs_lo = CAUSAL ? kb0 / kBQ : 0;
-  const int nsteps = nqs - qs_lo;
-  auto q0_of = [&](int j) { return (nqs - 1 - j) * kBQ; };
+  const int nsteps = (nqs - qs_lo) * group;
+  const int q_hi = (nqs - 1) * kBQ, q_lo = qs_lo * kBQ;
+  // query block after q0 in step order (wrapping to the next head's last)
+  auto next_q0 = [&](int q0) { return q0 == q_lo ? q_hi : q0 - kBQ; };
   // Buffer j % 3 of the three (chosen at run time: one set of lane offsets
   // then serves all three buffers).
   auto bufQ = [&](int j) -> uint16_t* { const int b = j % 3; return b == 0 ? sQ0 : (b == 1 ? sQ1 : sQ2); };
   auto bufO = [&](int j) -> uint16_t* { const int b = j % 3; return b == 0 ? sO0 : (b == 1 ? sO1 : sO2); };
   auto bufLD = [&](int j) -> float* { const int b = j % 3; return b == 0 ? sLD0 : (b == 1 ? sLD1 : sLD2); };
+  // The loads walk the steps with a cursor (query block, head bases), which
+  // spares a division per step.
+  int ld_q0 = q_hi;
+  const uint16_t* ld_q = Qg + b * sq.b + (long long)(hk * group) * sq.h;
+  const uint16_t* ld_o = dOg + b * sdo.b + (long long)(hk * group) * sdo.h;
+  size_t ld_row = ((size_t)b * H + hk * group) * N;  // LSE / D row of the head
   auto issue_loads = [&](int j) __attribute__((always_inline)) {
-    load_tile_async<D, kBQ, 256, true>(bufQ(j), Qh, q0_of(j), N, tid);
-    load_tile_async<D, kBQ, 256, true>(bufO(j), dOh, q0_of(j), N, tid);
-    if (w == 0) load_ld_async(bufLD(j), lse_h, d_h, q0_of(j), N, lane);
+    load_tile_async<D, kBQ, 256, true>(bufQ(j), ld_q, sq.n, ld_q0, N, tid);
+    load_tile_async<D, kBQ, 256, true>(bufO(j), ld_o, sdo.n, ld_q0, N, tid);
+    if (w == 0) load_ld_async(bufLD(j), LSEg + ld_row, Dg + ld_row, ld_q0, N, lane);
+    if (ld_q0 == q_lo) {
+      ld_q += sq.h;
+      ld_o += sdo.h;
+      ld_row += N;
+    }
+    ld_q0 = next_q0(ld_q0);
   };
   // A step needs the mask when some (key, query) pair of this wave is not
   // visible: causal diagonal, ragged query block, ragged key block.
-  auto needs_mask = [&](int j) {
-    const int q0 = q0_of(j);
+  auto needs_mask = [&](int q0) {
     return (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N) || (q0 + kBQ > N);
   };
 
@@ -136,13 +153,13 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
   bf16x8 kf[KS], vf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+    u32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
     if (key_l < N) {
-      a = *(const u32x4*)(Kg + head + (size_t)key_l * D + ks * 16 + hi * 8);
-      b = *(const u32x4*)(Vg + head + (size_t)key_l * D + ks * 16 + hi * 8);
+      a = *(const u32x4*)(Kh + (size_t)key_l * sk.n + ks * 16 + hi * 8);
+      c = *(const u32x4*)(Vh + (size_t)key_l * sv.n + ks * 16 + hi * 8);
     }
     kf[ks] = as_bf16x8(a);
-    vf[ks] = as_bf16x8(b);
+    vf[ks] = as_bf16x8(c);
   }
 
   f32x16 dk[DB], dv[DB];
@@ -226,12 +243,12 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
   {
     f32x16 s, dp;
     s_dp(sQ0, sO0, s, dp);
-    if (needs_mask(0)) {
+    if (needs_mask(q_hi)) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) p_ds_part(s, dp, sLD0, q0_of(0), g4, pP, pS, std::true_type{});
+      for (int g4 = 0; g4 < 4; ++g4) p_ds_part(s, dp, sLD0, q_hi, g4, pP, pS, std::true_type{});
     } else {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) p_ds_part(s, dp, sLD0, q0_of(0), g4, pP, pS, std::false_type{});
+      for (int g4 = 0; g4 < 4; ++g4) p_ds_part(s, dp, sLD0, q_hi, g4, pP, pS, std::false_type{});
     }
   }
 
@@ -239,14 +256,13 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
   // the P / dS work of step j+1 interleaved between them (matrix core and
   // vector ALU busy at once); the loads of step j+2 go to the third buffer
   // meanwhile.
-  auto iteration = [&](int j, auto masked_tag) __attribute__((always_inline)) {
+  auto iteration = [&](int j, int nq0, auto masked_tag) __attribute__((always_inline)) {
     f32x16 s, dp;
     s_dp(bufQ(j + 1), bufO(j + 1), s, dp);
     u32x4 nP[2], nS[2];
     const float* nLD = bufLD(j + 1);
     const uint16_t* cQ = bufQ(j);
     const uint16_t* cO = bufO(j);
-    const int nq0 = q0_of(j + 1);
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
@@ -277,14 +293,16 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
       __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU
     }
   };
+  int nq0 = q_hi;  // query block of step j + 1 (after the update below)
   for (int j = 0; j + 1 < nsteps; ++j) {
     pin_acc();
     wait_loads_and_sync();  // step j+1 landed; every wave is done with step j-1's buffer
     if (j + 2 < nsteps) issue_loads(j + 2);
-    if (needs_mask(j + 1))
-      iteration(j, std::true_type{});
+    nq0 = next_q0(nq0);
+    if (needs_mask(nq0))
+      iteration(j, nq0, std::true_type{});
     else
-      iteration(j, std::false_type{});
+      iteration(j, nq0, std::false_type{});
     pin_acc();
   }
   // last step: dV / dK only
@@ -302,9 +320,8 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
     for (int i = 0; i < 16; ++i) {
       const int key = kw0 + 8 * (i / 4) + 4 * hi + (i % 4);
       if (key < N) {
-        const size_t off = head + (size_t)key * D + d;
-        dKg[off] = (uint16_t)(pack_bf16x2(dk[db][i] * scale, 0.f) & 0xffffu);
-        dVg[off] = (uint16_t)(pack_bf16x2(dv[db][i], 0.f) & 0xffffu);
+        dKg[b * sdk.b + hk * sdk.h + (size_t)key * sdk.n + d] = (uint16_t)(pack_bf16x2(dk[db][i] * scale, 0.f) & 0xffffu);
+        dVg[b * sdv.b + hk * sdv.h + (size_t)key * sdv.n + d] = (uint16_t)(pack_bf16x2(dv[db][i], 0.f) & 0xffffu);
       }
     }
   }
@@ -315,14 +332,15 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
 template <int D, bool CAUSAL>
 static int launch(const BwdArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
-  const int BH = a.B * a.H;
-  const long long rows = (long long)BH * a.N;
+  const long long rows = (long long)a.B * a.H * a.N;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a.o, a.dO,
-                     a.delta, rows);
+                     a.delta, rows, a.H, a.N, a.so, a.sdo);
   const int nkb = (a.N + kBKC - 1) / kBKC;
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * BH)), dim3(256), 0, st, a.q, a.k, a.v,
-                     a.dO, a.lse, a.delta, a.dk, a.dv, BH, a.N, nkb, a.scale, a.scale * kLog2e);
+  const int BHkv = a.B * a.Hkv;
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * BHkv)), dim3(256), 0, st, a.q, a.k, a.v,
+                     a.dO, a.lse, a.delta, a.dk, a.dv, BHkv, a.H, a.H / a.Hkv, a.N, nkb, a.scale,
+                     a.scale * kLog2e, a.sq, a.sk, a.sv, a.sdo, a.sdk, a.sdv);
   if (hipGetLastError() != hipSuccess) return 1;
   return launch_bwd_dq(a);
 }

@@ -31,7 +31,8 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kQThreads, 1)
 dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
           const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
-          uint16_t* __restrict__ dQg, int BH, int N, int nqb, float scale, float scale_log2) {
+          uint16_t* __restrict__ dQg, int BH, int H, int group, int N, int nqb, float scale, float scale_log2,
+          Strides sq, Strides sk, Strides sv, Strides sdo, Strides sdq) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = kQBC * D;
@@ -48,9 +49,9 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
   const int wid = xcd_work_id(nqb * BH);
   const int bh = wid / nqb;
   const int qblk = CAUSAL ? nqb - 1 - (wid % nqb) : (wid % nqb);
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Kh = Kg + head;
-  const uint16_t* Vh = Vg + head;
+  const int b = bh / H, h = bh % H, hk = h / group;  // query head h reads K/V head h / group
+  const uint16_t* Kh = Kg + b * sk.b + hk * sk.h;
+  const uint16_t* Vh = Vg + b * sv.b + hk * sv.h;
   const int qw0 = qblk * kQBR + w * 32;
   const int qrow = qw0 + l32;
 
@@ -58,20 +59,20 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
   const int ntiles = (kend + kQBC - 1) / kQBC;
   const int wlast = CAUSAL ? min(ntiles - 1, (qw0 + 31) / kQBC) : ntiles - 1;
 
-  load_tile_async<D, kQBC, kQThreads, true>(sK0, Kh, 0, N, tid);
-  load_tile_async<D, kQBC, kQThreads, true>(sV0, Vh, 0, N, tid);
+  load_tile_async<D, kQBC, kQThreads, true>(sK0, Kh, sk.n, 0, N, tid);
+  load_tile_async<D, kQBC, kQThreads, true>(sV0, Vh, sv.n, 0, N, tid);
 
   // Q and dO as B operands of S^T = K Q^T and dP^T = V dO^T
   bf16x8 qf[KS], of[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+    u32x4 a = {0, 0, 0, 0}, e = {0, 0, 0, 0};
     if (qrow < N) {
-      a = *(const u32x4*)(Qg + head + (size_t)qrow * D + ks * 16 + hi * 8);
-      b = *(const u32x4*)(dOg + head + (size_t)qrow * D + ks * 16 + hi * 8);
+      a = *(const u32x4*)(Qg + b * sq.b + h * sq.h + (size_t)qrow * sq.n + ks * 16 + hi * 8);
+      e = *(const u32x4*)(dOg + b * sdo.b + h * sdo.h + (size_t)qrow * sdo.n + ks * 16 + hi * 8);
     }
     qf[ks] = as_bf16x8(a);
-    of[ks] = as_bf16x8(b);
+    of[ks] = as_bf16x8(e);
   }
   // rows past N: L = +inf gives P = 0
   const float Lq = qrow < N ? LSEg[(size_t)bh * N + qrow] * kLog2e : INFINITY;
@@ -140,8 +141,8 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
     const bool odd = t & 1;
     wait_loads_and_sync();  // tile t landed; every wave finished tile t-1
     if (t + 1 < ntiles) {
-      load_tile_async<D, kQBC, kQThreads, true>(odd ? sK0 : sK1, Kh, (t + 1) * kQBC, N, tid);
-      load_tile_async<D, kQBC, kQThreads, true>(odd ? sV0 : sV1, Vh, (t + 1) * kQBC, N, tid);
+      load_tile_async<D, kQBC, kQThreads, true>(odd ? sK0 : sK1, Kh, sk.n, (t + 1) * kQBC, N, tid);
+      load_tile_async<D, kQBC, kQThreads, true>(odd ? sV0 : sV1, Vh, sv.n, (t + 1) * kQBC, N, tid);
     }
     if (t > wlast) continue;  // this wave's rows see none of these keys
     const int k0 = t * kQBC;
@@ -155,7 +156,7 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
 
   // ---- dQ = scale dQ^T^T, bf16 (lane = query, d over the accumulator rows)
   if (qrow < N) {
-    uint16_t* row = dQg + head + (size_t)qrow * D;
+    uint16_t* row = dQg + b * sdq.b + h * sdq.h + (size_t)qrow * sdq.n;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -173,7 +174,8 @@ static int launch_dq(const BwdArgs& a) {
   const int BH = a.B * a.H;
   const int nqb = (a.N + kQBR - 1) / kQBR;
   hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb * BH)), dim3(kQThreads), 0, (hipStream_t)a.stream,
-                     a.q, a.k, a.v, a.dO, a.lse, a.delta, a.dq, BH, a.N, nqb, a.scale, a.scale * kLog2e);
+                     a.q, a.k, a.v, a.dO, a.lse, a.delta, a.dq, BH, a.H, a.H / a.Hkv, a.N, nqb, a.scale,
+                     a.scale * kLog2e, a.sq, a.sk, a.sv, a.sdo, a.sdq);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

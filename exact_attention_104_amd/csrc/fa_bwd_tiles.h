@@ -23,12 +23,14 @@ __device__ __forceinline__ int toff(int row, int col) {
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
 
-// Direct global->LDS loads of a [ROWS x D] bf16 tile (rows clamped to N-1) by
+// Direct global->LDS loads of a [ROWS x D] bf16 tile (row stride rs elements,
+// rows clamped to N-1) by
 // THREADS threads into the layout of toff<D> (TR) or of the forward's K tile.
 // Thread `tid` fills the 16-byte LDS chunks n * THREADS + tid; the source chunk
 // is chosen so that LDS holds the swizzled layout.
 template <int D, int ROWS, int THREADS, bool TR>
-__device__ __forceinline__ void load_tile_async(uint16_t* lds_tile, const uint16_t* head, int r0, int N, int tid) {
+__device__ __forceinline__ void load_tile_async(uint16_t* lds_tile, const uint16_t* head, long long rs, int r0, int N,
+                                                int tid) {
   constexpr int CH = D / 8;
   const int w = tid >> 6;
 #pragma unroll
@@ -37,7 +39,7 @@ __device__ __forceinline__ void load_tile_async(uint16_t* lds_tile, const uint16
     const int r = e / CH, p = e % CH;
     const int c = p ^ (TR ? swz2<D>(r) : swz_k<D>(r));
     const int row = min(r0 + r, N - 1);
-    const uint16_t* src = head + (size_t)row * D + c * 8;
+    const uint16_t* src = head + (uint64_t)(uint32_t)row * (uint32_t)rs + c * 8;  // rs < 2^31
     lds_dma16(lds_tile + (n * THREADS + w * 64) * 8, src);  // lane l lands at +16 l bytes
   }
 }

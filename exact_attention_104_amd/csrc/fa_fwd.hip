@@ -43,8 +43,8 @@ constexpr float kRescaleSlack = FA_RESCALE_SLACK;  // log2 units; P stays <= 256
 // so that LDS holds the XOR-swizzled layout. Rows past the end are read from
 // row N-1 (finite values that are masked, or multiplied by P = 0).
 template <int D, bool IS_V>
-__device__ __forceinline__ void load_tile_async(uint16_t* lds_tile, const uint16_t* head, int k0, int N,
-                                                int tid) {
+__device__ __forceinline__ void load_tile_async(uint16_t* lds_tile, const uint16_t* head, long long rs, int k0,
+                                                int N, int tid) {
   constexpr int CH = D / 8;
   const int w = tid >> 6;
 #pragma unroll
@@ -53,7 +53,7 @@ __device__ __forceinline__ void load_tile_async(uint16_t* lds_tile, const uint16
     const int r = e / CH, p = e % CH;
     const int c = p ^ (IS_V ? swz_v<D>(r) : swz_k<D>(r));
     const int row = min(k0 + r, N - 1);
-    const uint16_t* src = head + (size_t)row * D + c * 8;
+    const uint16_t* src = head + (uint64_t)(uint32_t)row * (uint32_t)rs + c * 8;  // rs < 2^31
     lds_dma16(lds_tile + (n * kThreads + w * 64) * 8, src);  // lane l lands at +16 l bytes
   }
 }
@@ -69,7 +69,8 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 1)
 fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
            const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og, float* __restrict__ LSEg,
-           int BH, int N, int nqb, float scale_log2) {
+           int BH, int H, int group, int N, int nqb, float scale_log2, Strides sq, Strides sk, Strides sv,
+           Strides so) {
   constexpr int KS = D / 16;        // k-steps of the S product
   constexpr int DB = D / 32;        // 32-row d blocks of O^T
   constexpr int TILE = kBC * D;     // elements of one K or V tile
@@ -93,9 +94,10 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   if ((total & 7) == 0) wid = (wid & 7) * (total >> 3) + (wid >> 3);
   const int bh = wid / nqb;
   const int qblk = CAUSAL ? nqb - 1 - (wid % nqb) : (wid % nqb);
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t* Kh = Kg + head;
-  const uint16_t* Vh = Vg + head;
+  const int b = bh / H, h = bh % H, hk = h / group;  // query head h reads K/V head h / group
+  const uint16_t* Qh = Qg + b * sq.b + h * sq.h;
+  const uint16_t* Kh = Kg + b * sk.b + hk * sk.h;
+  const uint16_t* Vh = Vg + b * sv.b + hk * sv.h;
   const int qw0 = qblk * kBR + w * kQW;  // first query row of this wave
   const int qrow = qw0 + l32;            // this lane's query
 
@@ -104,15 +106,15 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // last tile this wave needs (causal: the one holding its diagonal)
   const int wlast = CAUSAL ? min(ntiles - 1, (qw0 + kQW - 1) / kBC) : ntiles - 1;
 
-  load_tile_async<D, false>(sK0, Kh, 0, N, tid);
-  load_tile_async<D, true>(sV0, Vh, 0, N, tid);
+  load_tile_async<D, false>(sK0, Kh, sk.n, 0, N, tid);
+  load_tile_async<D, true>(sV0, Vh, sv.n, 0, N, tid);
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[q][16 ks + 8 hi .. +7].
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 u = {0, 0, 0, 0};
-    if (qrow < N) u = *(const u32x4*)(Qg + head + (size_t)qrow * D + ks * 16 + hi * 8);
+    if (qrow < N) u = *(const u32x4*)(Qh + (size_t)qrow * sq.n + ks * 16 + hi * 8);
     qf[ks] = as_bf16x8(u);
   }
 
@@ -125,8 +127,8 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   auto tile = [&](int t, const uint16_t* sK, const uint16_t* sV, uint16_t* nK, uint16_t* nV) {
     wait_loads_and_sync();  // tile t landed; every wave finished tile t-1
     if (t + 1 < ntiles) {
-      load_tile_async<D, false>(nK, Kh, (t + 1) * kBC, N, tid);
-      load_tile_async<D, true>(nV, Vh, (t + 1) * kBC, N, tid);
+      load_tile_async<D, false>(nK, Kh, sk.n, (t + 1) * kBC, N, tid);
+      load_tile_async<D, true>(nV, Vh, sv.n, (t + 1) * kBC, N, tid);
     }
     if (t > wlast) return;  // this wave's rows see none of these keys
     const int k0 = t * kBC;
@@ -236,7 +238,7 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   const float lt = l + other_half(l);
   const float inv = 1.0f / lt;
   if (qrow < N) {
-    uint16_t* orow = Og + head + (size_t)qrow * D;
+    uint16_t* orow = Og + b * so.b + h * so.h + (size_t)qrow * so.n;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -256,7 +258,8 @@ static int launch(const FwdArgs& a) {
   const int BH = a.B * a.H;
   const dim3 grid((unsigned)(nqb * BH)), block(kThreads);
   hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), grid, block, 0, (hipStream_t)a.stream,
-                     a.q, a.k, a.v, a.o, a.lse, BH, a.N, nqb, a.scale * kLog2e);
+                     a.q, a.k, a.v, a.o, a.lse, BH, a.H, a.H / a.Hkv, a.N, nqb, a.scale * kLog2e, a.sq, a.sk, a.sv,
+                     a.so);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

@@ -7,14 +7,25 @@
 
 namespace fa {
 
+// Element strides of a [B, H, N, d] tensor view whose d elements are contiguous.
+struct Strides {
+  long long b, h, n;
+};
+inline Strides contiguous_strides(int H, int N, int d) {
+  return Strides{(long long)H * N * d, (long long)N * d, (long long)d};
+}
+
+// H query heads share Hkv key/value heads: query head h reads K/V head
+// h / (H / Hkv) (Hkv divides H; Hkv = H is plain multi-head attention).
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
-  float* lse;
-  int B, H, N, d, causal;
+  float* lse;  // contiguous [B, H, N]
+  int B, H, Hkv, N, d, causal;
   float scale;
+  Strides sq, sk, sv, so;
   void* stream;
 };
 
@@ -24,13 +35,14 @@ struct BwdArgs {
   const uint16_t* v;
   const uint16_t* o;
   const uint16_t* dO;
-  const float* lse;
+  const float* lse;  // contiguous [B, H, N]
   uint16_t* dq;
-  uint16_t* dk;
+  uint16_t* dk;      // [B, Hkv, N, d] view: the sum over the query heads of each group
   uint16_t* dv;
-  float* delta;  // workspace: fp32 [B, H, N]
-  int B, H, N, d, causal;
+  float* delta;      // workspace: fp32 [B, H, N]
+  int B, H, Hkv, N, d, causal;
   float scale;
+  Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   void* stream;
 };
 

@@ -14,6 +14,9 @@ Recipe (one numpy ``Generator(PCG64(seed))`` per workload):
    20 in float32;
 3. round each tensor to bf16 (round to nearest even, via torch's CPU cast).
 
+Grouped heads (``grouped_inputs``): the same recipe without outliers, with K and
+V drawn ``[B, H_kv, N, d]``.
+
 Arrays are returned as float32 holding exact bf16 values. Hadamard signs are
 128 Rademacher draws (int8 +-1) from ``Generator(PCG64(1105))``.
 """
@@ -59,6 +62,14 @@ def attention_inputs(B: int, H: int, N: int, d: int, seed: int, with_do: bool = 
             pos = rng.choice(flat.size, size=count, replace=False)
             flat[pos] = flat[pos] * np.float32(20.0)
     return {n: to_bf16_values(raw[n]) for n in names}
+
+
+def grouped_inputs(B: int, H: int, H_kv: int, N: int, d: int, seed: int, with_do: bool = False) -> dict:
+    """Q (and dO) [B, H, N, d] with K, V [B, H_kv, N, d]; float32 exact bf16 values."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    heads = {"q": H, "k": H_kv, "v": H_kv, "do": H}
+    names = ["q", "k", "v"] + (["do"] if with_do else [])
+    return {n: to_bf16_values(rng.standard_normal((B, heads[n], N, d), dtype=np.float32)) for n in names}
 
 
 def hadamard_signs(seed: int = HADAMARD_SEED) -> np.ndarray:

@@ -38,20 +38,30 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL */
-  FA_ERR_SHAPE = 2,     /* B, H or N < 1, or the tensor is too large */
+  FA_ERR_SHAPE = 2,     /* B, H or N < 1, the tensor is too large, or H_kv does not divide H */
   FA_ERR_HEADDIM = 3,   /* d not supported (or rotation requested with d != 128) */
-  FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned, or a stride not a multiple of 8 */
   FA_ERR_WORKSPACE = 5, /* backward workspace NULL, misaligned or too small */
   FA_ERR_DEVICE = 6,    /* no HIP device, or the current device is not gfx950 */
-  FA_ERR_ALIAS = 7,     /* an output overlaps an input or another output */
+  FA_ERR_ALIAS = 7,     /* an output overlaps an input, another output or itself */
   FA_ERR_LAUNCH = 8,    /* the kernel launch failed (hipGetLastError) */
-  FA_ERR_ARG = 9        /* causal not 0/1, or scale not finite and positive */
+  FA_ERR_ARG = 9        /* causal not 0/1, scale not finite and positive, a stride < 1, or a row stride >= 2^31 */
 };
+
+/*
+ * Element strides of one [B, H, N, d] tensor view whose d elements are
+ * contiguous: element (b, h, n, j) is at base + b*batch + h*head + n*row + j.
+ * Contiguous [B, H, N, d] is {H*N*d, N*d, d}; [B, N, H, d] viewed as
+ * [B, H, N, d] is {N*H*d, d, H*d}.
+ */
+typedef struct fa_strides {
+  int64_t batch, head, row;
+} fa_strides;
 
 /* Human-readable name of a status (static string, never NULL). */
 const char* fa_status_string(int status);
@@ -71,6 +81,24 @@ int fa_abi_version(void);
  */
 int fa_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
            int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * fa_fwd on strided views, with grouped key/value heads (GQA; MQA when
+ * H_kv = 1): query head h attends to key/value head h / (H / H_kv)
+ * ([LIB] "Cases where FlashAttention does not help": GQA/MQA natively
+ * supported; [LIB] "FA2": models with aggressive GQA). fa_fwd is the case
+ * H_kv = H with contiguous strides.
+ *   q, o  : [B, H, N, d] views;  k, v : [B, H_kv, N, d] views
+ *   lse   : out, fp32 contiguous [B, H, N]
+ *   st    : host array of 4 views' strides, in order q, k, v, o; every
+ *           stride >= 1 and a multiple of 8 elements (rows start on 16-byte
+ *           boundaries), row strides below 2^31 (else FA_ERR_ARG); o must
+ *           not overlap itself (FA_ERR_ALIAS)
+ *   H_kv  : divides H (else FA_ERR_SHAPE)
+ */
+int fa_fwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                   int B, int H, int H_kv, int N, int d, const fa_strides* st, int causal, float scale,
+                   void* stream);
 
 /*
  * Bytes of device workspace fa_bwd needs: the fp32 row vector
@@ -96,6 +124,23 @@ int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16
            const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
            int B, int H, int N, int d, int causal, float scale, void* ws, size_t ws_bytes,
            void* stream);
+
+/*
+ * fa_bwd on strided views with grouped key/value heads (see fa_fwd_strided):
+ * dK and dV of key/value head g are the sums over the H / H_kv query heads
+ * that read it (the chain rule through the shared head). fa_bwd is the case
+ * H_kv = H with contiguous strides. The workspace is fa_bwd_workspace_bytes
+ * (B, H, N, d) as for fa_bwd.
+ *   q, o, dO, dq : [B, H, N, d] views;  k, v, dk, dv : [B, H_kv, N, d] views
+ *   lse          : in, fp32 contiguous [B, H, N]
+ *   st           : host array of 8 views' strides, in order q, k, v, o, dO,
+ *                  dq, dk, dv (rules as in fa_fwd_strided; dq, dk, dv must
+ *                  not overlap themselves)
+ */
+int fa_bwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                   const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                   int B, int H, int H_kv, int N, int d, const fa_strides* st, int causal, float scale,
+                   void* ws, size_t ws_bytes, void* stream);
 
 /*
  * FP8 input path ([LIB] "FA3 — the Hopper moment", pillar 3; [LIN] "FA3

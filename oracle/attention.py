@@ -14,7 +14,8 @@ Definitions followed
   the partial output rescaled by the same factor; dividing by the final l is
   exact.
 * [LIB] section "Cases where FlashAttention does not help": the causal mask
-  is one of the masks the kernels ship.
+  is one of the masks the kernels ship; grouped-query and multi-query
+  attention (GQA/MQA) are supported natively.
 
 Readings where the pages are silent
 -----------------------------------
@@ -23,6 +24,11 @@ Readings where the pages are silent
 * Causal: query i sees key j iff j <= i (lower triangle, diagonal included,
   N_q == N_k), so no row is ever fully masked.
 * LSE uses the natural logarithm of the sum over the *scaled* scores.
+* GQA/MQA (the pages name them only): H query heads share H_kv key/value
+  heads, query head h reading key/value head h // (H // H_kv) (consecutive
+  query heads form a group). The forward is the multi-head definition with
+  each shared head repeated; the key/value gradients of a shared head are the
+  sums over its group (chain rule through the repetition).
 * Backward: the pages only say that P is recomputed from L. The gradients
   below are the derivative of the forward definition (chain rule through the
   softmax): dV = P^T dO, dP = dO V^T, D_i = sum_j P_ij dP_ij,
@@ -139,6 +145,30 @@ def backward(q, k, v, do, causal: bool = False, scale: float | None = None):
             dq[b, h], dk[b, h], dv[b, h] = backward_head(q[b, h], k[b, h], v[b, h], do[b, h],
                                                          causal, scale)
     return dq, dk, dv
+
+
+def expand_kv(x, H: int) -> np.ndarray:
+    """[B, H_kv, N, d] -> [B, H, N, d]: query head h sees key/value head h // (H // H_kv)."""
+    x = _f64(x)
+    Hkv = x.shape[1]
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("H_kv must divide H")
+    return np.repeat(x, H // Hkv, axis=1)
+
+
+def forward_gqa(q, k, v, causal: bool = False, scale: float | None = None):
+    """Forward with grouped key/value heads: k, v are [B, H_kv, N, d]."""
+    H = q.shape[1]
+    return forward(q, expand_kv(k, H), expand_kv(v, H), causal, scale)
+
+
+def backward_gqa(q, k, v, do, causal: bool = False, scale: float | None = None):
+    """Backward with grouped key/value heads: dK, dV summed over each group."""
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    dq, dk, dv = backward(q, expand_kv(k, H), expand_kv(v, H), do, causal, scale)
+    g = H // Hkv
+    return dq, dk.reshape(B, Hkv, g, N, d).sum(axis=2), dv.reshape(B, Hkv, g, N, d).sum(axis=2)
 
 
 def row_delta(o, do):

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_version_and_status_strings():
-    assert fa.abi_version() == 1
+    assert fa.abi_version() == 2
     codes = declared_status_codes()
     assert codes["FA_OK"] == 0 and len(codes) == 10
     for name, val in codes.items():
@@ -99,6 +99,70 @@ def test_bwd_quant_fp8_reject_bad_arguments():
     f8 = [P + i * 0x100000 for i in range(8)]
     assert lib.fa_fwd_fp8(*f8[:7], None, 1, 1, 64, 64, 0, 0.125, None) == 1
     assert lib.fa_fwd_fp8(*f8, 1, 1, 64, 80, 0, 0.125, None) == 3
+
+
+def _st(*triples):
+    arr = (fa.Strides * len(triples))()
+    for i, t in enumerate(triples):
+        arr[i] = fa.Strides(*t)
+    return arr
+
+
+def test_strided_entry_points_reject_bad_arguments():
+    """Every call below fails host validation before any HIP call."""
+    lib = fa.load_library()
+    B, H, N, d = 1, 4, 64, 64
+    c = (H * N * d, N * d, d)               # contiguous [B, H, N, d]
+    ckv = (2 * N * d, N * d, d)             # contiguous [B, 2, N, d]
+    q, k, v, o, lse = (P + i * 0x100000 for i in range(5))
+
+    def fwd(st, Hkv=2, **kw):
+        a = dict(q=q, k=k, v=v, o=o, lse=lse, B=B, H=H, Hkv=Hkv, N=N, d=d, st=st, causal=1, scale=0.125)
+        a.update(kw)
+        return lib.fa_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
+                                  a["d"], a["st"], a["causal"], a["scale"], None)
+    good = _st(c, ckv, ckv, c)
+    assert fwd(None) == 1                                   # no strides
+    assert fwd(good, Hkv=3) == 2                            # H_kv does not divide H
+    assert fwd(good, Hkv=0) == 2
+    assert fwd(_st(c, ckv, ckv, (c[0], c[1], 0))) == 9      # row stride 0
+    assert fwd(_st(c, (ckv[0], ckv[1], 1 << 31), ckv, c)) == 9  # row stride 2^31
+    assert fwd(_st(c, ckv, (ckv[0], ckv[1], d + 4), c)) == 4  # rows not on 16-byte boundaries
+    assert fwd(_st(c, ckv, ckv, (c[0], 8, d))) == 7         # o overlaps itself (heads 8 elements apart)
+    assert fwd(good, o=q) == 7                              # o aliases q
+    assert fwd(good, d=96) == 3
+    # [B, N, H, d] strides for q and o, grouped K/V: accepted up to the device check,
+    # which only a machine without a GPU reaches (see below)
+    bwd_st = _st(c, ckv, ckv, c, c, c, ckv, ckv)
+    ws = 0x40000000
+    ptrs = [P + i * 0x100000 for i in range(9)]
+    args = ptrs + [B, H, 2, N, d, bwd_st, 1, 0.125, ws, lib.fa_bwd_workspace_bytes(B, H, N, d), None]
+    bad = list(args)
+    bad[14] = None
+    assert lib.fa_bwd_strided(*bad) == 1
+    bad = list(args)
+    bad[11] = 3                                             # H_kv = 3 does not divide 4
+    assert lib.fa_bwd_strided(*bad) == 2
+    bad = list(args)
+    bad[14] = _st(c, ckv, ckv, c, c, c, (ckv[0], 8, d), ckv)  # dk overlaps itself
+    assert lib.fa_bwd_strided(*bad) == 7
+    bad = list(args)
+    bad[8] = ptrs[7]                                        # dv aliases dk
+    assert lib.fa_bwd_strided(*bad) == 7
+    bad = list(args)
+    bad[17] = ws + 8                                        # misaligned workspace
+    assert lib.fa_bwd_strided(*bad) == 5
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="valid-looking fake pointers must never reach a GPU")
+def test_strided_no_device_is_reported_after_validation():
+    lib = fa.load_library()
+    B, H, N, d = 2, 4, 64, 64
+    bnhd = (N * H * d, d, H * d)                            # [B, N, H, d] viewed as [B, H, N, d]
+    kv = (N * 2 * d, d, 2 * d)
+    st = _st(bnhd, kv, kv, bnhd)
+    ptrs = [P + i * 0x100000 for i in range(5)]
+    assert lib.fa_fwd_strided(*ptrs, B, H, 2, N, d, st, 1, 0.125, None) == 6
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="valid-looking fake pointers must never reach a GPU")

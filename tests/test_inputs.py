@@ -32,3 +32,16 @@ def test_signs_and_bits():
     assert np.array_equal(s, fa_inputs.hadamard_signs())
     v = np.array([1.0, -2.5, 0.0], dtype=np.float32)
     assert list(fa_inputs.bf16_bits(v)) == [0x3F80, 0xC020, 0x0000]
+
+
+def test_grouped_inputs():
+    a = fa_inputs.grouped_inputs(2, 8, 2, 33, 64, seed=9, with_do=True)
+    assert a["q"].shape == a["do"].shape == (2, 8, 33, 64)
+    assert a["k"].shape == a["v"].shape == (2, 2, 33, 64)
+    b = fa_inputs.grouped_inputs(2, 8, 2, 33, 64, seed=9, with_do=True)
+    for n in a:
+        assert np.array_equal(a[n], b[n]) and not (a[n].view(np.uint32) & 0xFFFF).any()
+    # with H_kv = H the draws are those of attention_inputs
+    c = fa_inputs.grouped_inputs(1, 2, 2, 10, 64, seed=3)
+    e = fa_inputs.attention_inputs(1, 2, 10, 64, seed=3)
+    assert all(np.array_equal(c[n], e[n]) for n in ("q", "k", "v"))

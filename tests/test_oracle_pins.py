@@ -115,6 +115,27 @@ def pin_torch_sdpa(causal, n=33, d=16):
     assert np.allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-10)
 
 
+def pin_torch_sdpa_gqa(causal, n=17, d=8):
+    """Grouped heads: torch's fp64 SDPA with enable_gqa (and its autograd) as the
+    independent reference for forward_gqa / backward_gqa; GQA (4 query heads on 2
+    key/value heads) and MQA (4 on 1)."""
+    scale = 1.0 / math.sqrt(d)
+    for hkv in (2, 1):
+        q, do = _rand((2, 4, n, d), 40), _rand((2, 4, n, d), 41)
+        k, v = _rand((2, hkv, n, d), 42), _rand((2, hkv, n, d), 43)
+        o, lse = A.forward_gqa(q, k, v, causal, scale)
+        dq, dk, dv = A.backward_gqa(q, k, v, do, causal, scale)
+        tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+        to = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, is_causal=causal, scale=float(np.float32(scale)), enable_gqa=True)
+        to.backward(torch.tensor(do, dtype=torch.float64))
+        assert dk.shape == k.shape and dv.shape == v.shape
+        assert np.allclose(o, to.detach().numpy(), rtol=1e-12, atol=1e-12)
+        assert np.allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-10)
+        assert np.allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-10)
+        assert np.allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-10)
+
+
 def pin_special_cases():
     # N = 1: O = V, LSE = s q.k
     q, k, v = _rand((1, 1, 1, 8), 30), _rand((1, 1, 1, 8), 31), _rand((1, 1, 1, 8), 32)
@@ -209,6 +230,18 @@ def test_p6_torch_sdpa_and_autograd(causal):
     pin_torch_sdpa(causal)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_p10_torch_sdpa_gqa(causal):
+    pin_torch_sdpa_gqa(causal)
+
+
+def test_gqa_with_all_heads_is_multi_head():
+    q, k, v = _rand((1, 3, 11, 8), 50), _rand((1, 3, 11, 8), 51), _rand((1, 3, 11, 8), 52)
+    o1, l1 = A.forward_gqa(q, k, v, True, 0.25)
+    o2, l2 = A.forward(q, k, v, True, 0.25)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 def test_p7_special_cases():
     pin_special_cases()
 
@@ -274,7 +307,23 @@ def _softmax_no_log(s):
     return p, m, np.exp(l)  # LSE would become m + l
 
 
+def _expand_kv_modulo(x, H):
+    """Wrong head mapping: query head h reads key/value head h % H_kv."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.tile(x, (1, H // x.shape[1], 1, 1))
+
+
+def _backward_gqa_first_head(q, k, v, do, causal=False, scale=None):
+    """Forgets the group sum: keeps only the first query head's dK, dV."""
+    B, H, N, d = q.shape
+    g = H // k.shape[1]
+    dq, dk, dv = A.backward(q, A.expand_kv(k, H), A.expand_kv(v, H), do, causal, scale)
+    return dq, dk[:, ::g], dv[:, ::g]
+
+
 @pytest.mark.parametrize("target,replacement,pins", [
+    ("expand_kv", _expand_kv_modulo, ["sdpa_gqa"]),
+    ("backward_gqa", _backward_gqa_first_head, ["sdpa_gqa"]),
     ("head_scores", _mask_off_by_one, ["zero_query", "sdpa", "special"]),
     ("head_scores", _scores_unscaled, ["sdpa", "lse", "golden_scale"]),
     ("backward_head", _backward_wrong_sign, ["fd", "sdpa"]),
@@ -296,6 +345,7 @@ def test_planted_mistakes_are_caught(monkeypatch, target, replacement, pins):
         "fd": lambda: pin_finite_differences(5, 2, True),
         "golden": pin_golden_closed_form,
         "golden_scale": lambda: pin_torch_sdpa(False, n=9, d=4),
+        "sdpa_gqa": lambda: pin_torch_sdpa_gqa(True, n=9, d=4),
     }
     for name in pins:
         with pytest.raises((AssertionError, ValueError, FloatingPointError)):

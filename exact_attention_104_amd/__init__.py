@@ -48,6 +48,7 @@ SIGNATURES = {
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _F, _P, ctypes.c_size_t, _P]),
     "fa_bwd_strided": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _P, _I, _F, _P, ctypes.c_size_t, _P]),
+    "fa_bwd_strided_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
     "fa_quant_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_fwd_fp8": (_I, [_P] * 8 + [_I, _I, _I, _I, _I, _F, _P]),
 }
@@ -172,8 +173,12 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     return o, lse_t
 
 
-def bwd_workspace_bytes(B, H, N, d) -> int:
-    return int(load_library().fa_bwd_workspace_bytes(B, H, N, d))
+def bwd_workspace_bytes(B, H, N, d, H_kv=None, causal=False) -> int:
+    """Workspace bytes of bwd: fa_bwd's, or with H_kv key/value heads fa_bwd_strided's."""
+    lib = load_library()
+    if H_kv is None:
+        return int(lib.fa_bwd_workspace_bytes(B, H, N, d))
+    return int(lib.fa_bwd_strided_workspace_bytes(B, H, H_kv, N, d, int(bool(causal))))
 
 
 def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, workspace=None):
@@ -188,11 +193,11 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, w
     for n, t in (("k", k), ("v", v)):
         _check_view(n, t, (B, Hkv, N, d))
     _check_tensor("lse", lse, torch.float32, (B, H, N))
-    need = bwd_workspace_bytes(B, H, N, d)
+    sc, c = _scale(scale, d), int(bool(causal))
+    need = int(lib.fa_bwd_strided_workspace_bytes(B, H, Hkv, N, d, c))
     ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
     _check_tensor("workspace", ws, torch.uint8)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    sc, c = _scale(scale, d), int(bool(causal))
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
     if Hkv == H and all(t.is_contiguous() for t in (q, k, v, o, do, dq, dk, dv)):

@@ -153,6 +153,13 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   return fa::bwd_delta_bytes(B, H, N);
 }
 
+size_t fa_bwd_strided_workspace_bytes(int B, int H, int H_kv, int N, int d, int causal) {
+  if ((d != 64 && d != 128) || !shape_ok(B, H, N, d) || H_kv < 1 || H % H_kv != 0) return 0;
+  if (causal != 0 && causal != 1) return 0;
+  const int split = fa::bwd_kv_split(B, H_kv, H / H_kv, N, causal);
+  return fa::bwd_delta_bytes(B, H, N) + fa::bwd_partial_bytes(B, H_kv, N, d, split);
+}
+
 int fa_bwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                    const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                    int B, int H, int H_kv, int N, int d, const fa_strides* st, int causal, float scale,
@@ -170,7 +177,7 @@ int fa_bwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, cons
   for (const View* x : all)
     if (!x->aligned()) return FA_ERR_ALIGN;
   if (!aligned16(lse)) return FA_ERR_ALIGN;
-  const size_t need = fa_bwd_workspace_bytes(B, H, N, d);
+  const size_t need = fa_bwd_strided_workspace_bytes(B, H, H_kv, N, d, causal);
   if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need) return FA_ERR_WORKSPACE;
   const size_t lb = (size_t)B * H * N * 4;
   const Range ins[6] = {vq.range(), vk.range(), vv.range(), vo.range(), vdo.range(), span(lse, lb)};
@@ -180,6 +187,8 @@ int fa_bwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, cons
   auto S = [&](int i) { return fa::Strides{st[i].batch, st[i].head, st[i].row}; };
   fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, (float*)ws, B, H, H_kv, N, d, causal, scale,
                 S(0), S(1), S(2), S(3), S(4), S(5), S(6), S(7), stream};
+  a.split = fa::bwd_kv_split(B, H_kv, H / H_kv, N, causal);
+  a.part = a.split > 1 ? (float*)((char*)ws + fa::bwd_delta_bytes(B, H, N)) : nullptr;
   return fa::launch_bwd(a) ? FA_ERR_LAUNCH : FA_OK;
 }
 

@@ -71,9 +71,9 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 1)
 dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
             const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
-            uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, int BHkv, int H, int group, int N, int nkb,
-            float scale, float scale_log2, Strides sq, Strides sk, Strides sv, Strides sdo, Strides sdk,
-            Strides sdv) {
+            uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, float* __restrict__ part, int BHkv, int H,
+            int group, int split, int N, int nkb, float scale, float scale_log2, Strides sq, Strides sk,
+            Strides sv, Strides sdo, Strides sdk, Strides sdv) {
   constexpr int KS = D / 16;    // k-steps over d
   constexpr int DB = D / 32;    // 32-wide d blocks
   constexpr int QT = kBQ * D;   // elements of a Q or dO tile
@@ -94,26 +94,29 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
   const int lane = tid & 63, w = tid >> 6;
 
   // One K/V head's key blocks run together on one XCD, heaviest causal block
-  // first. The block's keys serve the group query heads hk * group + g.
-  const int wid = xcd_work_id(nkb * BHkv);
-  const int bhk = wid / nkb;
+  // first. The block's keys serve the group's query heads hk * group + g;
+  // with split > 1, workgroup si of the key block takes the gs = group / split
+  // heads from hk * group + si * gs and leaves fp32 partials.
+  const int wid = xcd_work_id(nkb * BHkv * split);
+  const int unit = wid / nkb;  // (bhk, si)
   const int kblk = wid % nkb;
-  const int Hkv = H / group;
+  const int bhk = unit / split, si = unit % split;
+  const int Hkv = H / group, gs = group / split;
   const int b = bhk / Hkv, hk = bhk % Hkv;
+  const int h0 = hk * group + si * gs;  // first query head of this workgroup
   const uint16_t* Kh = Kg + b * sk.b + hk * sk.h;
   const uint16_t* Vh = Vg + b * sv.b + hk * sv.h;
   const int kb0 = kblk * kBKC;
   const int kw0 = kb0 + w * 32;
   const int key_l = kw0 + (lane & 31);  // this lane's key in S / dP
 
-  // Steps run over the group's query heads hk * group + 0 .. group - 1 in
-  // turn; within a head, from the last query block down (so that the
+  // Steps run over the query heads h0 .. h0 + gs - 1 in turn; within a head, from the last query block down (so that the
   // concurrent key blocks of a head read the same Q / dO tiles at about the
   // same time) to block qs_lo (causal: blocks below the key block are all
   // masked).
   const int nqs = (N + kBQ - 1) / kBQ;
   const int qs_lo = CAUSAL ? kb0 / kBQ : 0;
-  const int nsteps = (nqs - qs_lo) * group;
+  const int nsteps = (nqs - qs_lo) * gs;
   const int q_hi = (nqs - 1) * kBQ, q_lo = qs_lo * kBQ;
   // query block after q0 in step order (wrapping to the next head's last)
   auto next_q0 = [&](int q0) { return q0 == q_lo ? q_hi : q0 - kBQ; };
@@ -125,9 +128,9 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
   // The loads walk the steps with a cursor (query block, head bases), which
   // spares a division per step.
   int ld_q0 = q_hi;
-  const uint16_t* ld_q = Qg + b * sq.b + (long long)(hk * group) * sq.h;
-  const uint16_t* ld_o = dOg + b * sdo.b + (long long)(hk * group) * sdo.h;
-  size_t ld_row = ((size_t)b * H + hk * group) * N;  // LSE / D row of the head
+  const uint16_t* ld_q = Qg + b * sq.b + (long long)h0 * sq.h;
+  const uint16_t* ld_o = dOg + b * sdo.b + (long long)h0 * sdo.h;
+  size_t ld_row = ((size_t)b * H + h0) * N;  // LSE / D row of the head
   auto issue_loads = [&](int j) __attribute__((always_inline)) {
     load_tile_async<D, kBQ, 256, true>(bufQ(j), ld_q, sq.n, ld_q0, N, tid);
     load_tile_async<D, kBQ, 256, true>(bufO(j), ld_o, sdo.n, ld_q0, N, tid);
@@ -312,19 +315,76 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
 #pragma unroll
     for (int db = 0; db < DB; ++db) dvdk_part(bufQ(nsteps - 1), bufO(nsteps - 1), s2, db);
 
-  // ---- dK (times scale) and dV, bf16 (lane = d column, 16 keys per lane)
+  // ---- dK (times scale) and dV, bf16 (lane = d column, 16 keys per lane);
+  // with split > 1, the unscaled fp32 sums into this workgroup's partials
+  if (split == 1) {
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    const int d = db * 32 + l32;
+    for (int db = 0; db < DB; ++db) {
+      const int d = db * 32 + l32;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kw0 + 8 * (i / 4) + 4 * hi + (i % 4);
-      if (key < N) {
-        dKg[b * sdk.b + hk * sdk.h + (size_t)key * sdk.n + d] = (uint16_t)(pack_bf16x2(dk[db][i] * scale, 0.f) & 0xffffu);
-        dVg[b * sdv.b + hk * sdv.h + (size_t)key * sdv.n + d] = (uint16_t)(pack_bf16x2(dv[db][i], 0.f) & 0xffffu);
+      for (int i = 0; i < 16; ++i) {
+        const int key = kw0 + 8 * (i / 4) + 4 * hi + (i % 4);
+        if (key < N) {
+          dKg[b * sdk.b + hk * sdk.h + (size_t)key * sdk.n + d] =
+              (uint16_t)(pack_bf16x2(dk[db][i] * scale, 0.f) & 0xffffu);
+          dVg[b * sdv.b + hk * sdv.h + (size_t)key * sdv.n + d] = (uint16_t)(pack_bf16x2(dv[db][i], 0.f) & 0xffffu);
+        }
+      }
+    }
+  } else {
+    float* pk = part + (size_t)unit * N * D;
+    float* pv = pk + (size_t)BHkv * split * N * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = db * 32 + l32;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kw0 + 8 * (i / 4) + 4 * hi + (i % 4);
+        if (key < N) {
+          pk[(size_t)key * D + d] = dk[db][i];
+          pv[(size_t)key * D + d] = dv[db][i];
+        }
       }
     }
   }
+}
+
+// dK = scale * (sum of the split partials), dV = sum, to bf16 views. One
+// thread per 8 consecutive elements of a (batch, K/V head, key) row.
+template <int D>
+__global__ void __launch_bounds__(256)
+kv_reduce_kernel(const float* __restrict__ part, uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg,
+                 long long rows, int Hkv, int split, int N, float scale, Strides sdk, Strides sdv) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  if (row >= rows) return;
+  const int c = threadIdx.x % LPR;
+  const long long bhk = row / N;
+  const int n = (int)(row % N), b = (int)(bhk / Hkv), hk = (int)(bhk % Hkv);
+  const size_t half = (size_t)rows * split * D;  // dV partials follow the dK partials
+  float sk[8] = {}, sv[8] = {};
+  for (int si = 0; si < split; ++si) {
+    const float* src = part + ((size_t)(bhk * split + si) * N + n) * D + c * 8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 a = *(const f32x4*)(src + 4 * h);
+      const f32x4 e = *(const f32x4*)(src + half + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sk[4 * h + j] += a[j];
+        sv[4 * h + j] += e[j];
+      }
+    }
+  }
+  u32x4 ok, ov;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ok[j] = pack_bf16x2(sk[2 * j] * scale, sk[2 * j + 1] * scale);
+    ov[j] = pack_bf16x2(sv[2 * j], sv[2 * j + 1]);
+  }
+  *(u32x4*)(dKg + b * sdk.b + hk * sdk.h + (long long)n * sdk.n + c * 8) = ok;
+  *(u32x4*)(dVg + b * sdv.b + hk * sdv.h + (long long)n * sdv.n + c * 8) = ov;
 }
 
 
@@ -336,12 +396,19 @@ static int launch(const BwdArgs& a) {
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a.o, a.dO,
                      a.delta, rows, a.H, a.N, a.so, a.sdo);
-  const int nkb = (a.N + kBKC - 1) / kBKC;
+  const int nkb = bwd_key_blocks(a.N);
+  static_assert(kBKC == 128, "bwd_key_blocks assumes 128-key blocks");
   const int BHkv = a.B * a.Hkv;
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * BHkv)), dim3(256), 0, st, a.q, a.k, a.v,
-                     a.dO, a.lse, a.delta, a.dk, a.dv, BHkv, a.H, a.H / a.Hkv, a.N, nkb, a.scale,
-                     a.scale * kLog2e, a.sq, a.sk, a.sv, a.sdo, a.sdk, a.sdv);
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * BHkv * a.split)), dim3(256), 0, st, a.q, a.k,
+                     a.v, a.dO, a.lse, a.delta, a.dk, a.dv, a.part, BHkv, a.H, a.H / a.Hkv, a.split, a.N, nkb,
+                     a.scale, a.scale * kLog2e, a.sq, a.sk, a.sv, a.sdo, a.sdk, a.sdv);
   if (hipGetLastError() != hipSuccess) return 1;
+  if (a.split > 1) {
+    const long long kv_rows = (long long)BHkv * a.N;
+    hipLaunchKernelGGL((kv_reduce_kernel<D>), dim3((unsigned)((kv_rows + RPB - 1) / RPB)), dim3(256), 0, st,
+                       a.part, a.dk, a.dv, kv_rows, a.Hkv, a.split, a.N, a.scale, a.sdk, a.sdv);
+    if (hipGetLastError() != hipSuccess) return 1;
+  }
   return launch_bwd_dq(a);
 }
 

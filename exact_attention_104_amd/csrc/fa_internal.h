@@ -39,11 +39,13 @@ struct BwdArgs {
   uint16_t* dq;
   uint16_t* dk;      // [B, Hkv, N, d] view: the sum over the query heads of each group
   uint16_t* dv;
-  float* delta;      // workspace: fp32 [B, H, N]
+  float* delta;      // workspace: fp32 D [B, H, N]
   int B, H, Hkv, N, d, causal;
   float scale;
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   void* stream;
+  float* part = nullptr;  // workspace after D: fp32 partial dK, dV when split > 1
+  int split = 1;          // bwd_kv_split
 };
 
 struct QuantArgs {
@@ -76,8 +78,30 @@ int launch_bwd_dq(const BwdArgs& a);  // the dQ launch alone (after D is written
 int launch_quant_fp8(const QuantArgs& a);
 int launch_fwd_fp8(const Fp8FwdArgs& a);
 
-// Workspace of the backward pass: D = rowsum(dO o O), rounded to 256 bytes.
+// Workspace of the backward pass: D = rowsum(dO o O), rounded to 256 bytes,
+// then (grouped heads split over workgroups only) fp32 partial dK, dV.
 inline size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline size_t bwd_delta_bytes(int B, int H, int N) { return round256((size_t)B * H * N * sizeof(float)); }
+
+// Key blocks per (batch, K/V head) in the dK/dV kernel (128 keys each).
+inline int bwd_key_blocks(int N) { return (N + 127) / 128; }
+
+// How many workgroups share one (batch, K/V head, key block) of grouped
+// heads: each sums the gradients of group / split query heads and, for
+// split > 1, writes fp32 partials that a reduction adds up. The smallest
+// divisor of the group that gives at least 256 workgroups (one per CU), or
+// 1024 when causal (so that the uneven causal blocks balance), else the
+// whole group.
+inline int bwd_kv_split(int B, int H_kv, int group, int N, int causal) {
+  const long long units = (long long)bwd_key_blocks(N) * B * H_kv;
+  const long long want = causal ? 1024 : 256;
+  for (int s = 1; s < group; ++s)
+    if (group % s == 0 && units * s >= want) return s;
+  return group;
+}
+
+inline size_t bwd_partial_bytes(int B, int H_kv, int N, int d, int split) {
+  return split > 1 ? round256((size_t)2 * B * H_kv * split * N * d * sizeof(float)) : 0;
+}
 
 }  // namespace fa

@@ -108,6 +108,17 @@ int fa_fwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /*
+ * Bytes of device workspace fa_bwd_strided needs: D as above, then, when the
+ * key/value heads are grouped (H_kv < H) and one workgroup per (batch, K/V
+ * head, 128-key block) would leave the GPU under-filled or, causal, unevenly
+ * loaded, fp32 partial dK and dV of the workgroups that share a key block:
+ * 2 x B x H_kv x s x N x d x 4 bytes for a split s dividing H / H_kv (at most
+ * 2 x B x H x N x d x 4). Equals fa_bwd_workspace_bytes when H_kv = H.
+ * Returns 0 for invalid arguments.
+ */
+size_t fa_bwd_strided_workspace_bytes(int B, int H, int H_kv, int N, int d, int causal);
+
+/*
  * Backward by recomputation: P_ij = exp(scale q_i.k_j - LSE_i) is rebuilt tile
  * by tile from the saved LSE ([HUB] "How it works"; [LIB] "FA1 — changing the
  * order of the operations"); dV = P^T dO, dP = dO V^T, D = rowsum(dO o O),
@@ -129,8 +140,8 @@ int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16
  * fa_bwd on strided views with grouped key/value heads (see fa_fwd_strided):
  * dK and dV of key/value head g are the sums over the H / H_kv query heads
  * that read it (the chain rule through the shared head). fa_bwd is the case
- * H_kv = H with contiguous strides. The workspace is fa_bwd_workspace_bytes
- * (B, H, N, d) as for fa_bwd.
+ * H_kv = H with contiguous strides. The workspace is
+ * fa_bwd_strided_workspace_bytes(B, H, H_kv, N, d, causal).
  *   q, o, dO, dq : [B, H, N, d] views;  k, v, dk, dv : [B, H_kv, N, d] views
  *   lse          : in, fp32 contiguous [B, H, N]
  *   st           : host array of 8 views' strides, in order q, k, v, o, dO,

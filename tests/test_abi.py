@@ -54,6 +54,22 @@ def test_workspace_bytes():
     assert lib.fa_bwd_workspace_bytes(0, 1, 3, 64) == 0
 
 
+def test_strided_workspace_bytes():
+    lib = fa.load_library()
+    for causal in (0, 1):  # H_kv = H: D only, as fa_bwd
+        assert lib.fa_bwd_strided_workspace_bytes(2, 16, 16, 4096, 128, causal) == 2 * 16 * 4096 * 4
+    # B=1, H=8, H_kv=2, N=256: 4 (batch, K/V head, key block) units, so the whole
+    # group of 4 is split: D + fp32 dK, dV partials of 2 x 1 x 2 x 4 x 256 x 64
+    assert lib.fa_bwd_strided_workspace_bytes(1, 8, 2, 256, 64, 1) == 8 * 256 * 4 + 2 * 2 * 4 * 256 * 64 * 4
+    # B=2, H=16, H_kv=2, N=8192: 256 units; causal splits the group of 8 in 4
+    assert lib.fa_bwd_strided_workspace_bytes(2, 16, 2, 8192, 128, 1) == \
+        2 * 16 * 8192 * 4 + 2 * 2 * 2 * 4 * 8192 * 128 * 4
+    assert lib.fa_bwd_strided_workspace_bytes(2, 16, 2, 8192, 128, 0) == 2 * 16 * 8192 * 4
+    assert lib.fa_bwd_strided_workspace_bytes(1, 8, 3, 256, 64, 1) == 0   # H_kv does not divide H
+    assert lib.fa_bwd_strided_workspace_bytes(1, 8, 2, 256, 64, 2) == 0   # causal not 0 / 1
+    assert lib.fa_bwd_strided_workspace_bytes(1, 8, 2, 256, 96, 0) == 0
+
+
 def _fwd(**kw):
     a = dict(q=P, k=P + 0x100000, v=P + 0x200000, o=P + 0x300000, lse=P + 0x400000,
              B=1, H=1, N=64, d=64, causal=0, scale=0.125, stream=None)
@@ -136,7 +152,7 @@ def test_strided_entry_points_reject_bad_arguments():
     bwd_st = _st(c, ckv, ckv, c, c, c, ckv, ckv)
     ws = 0x40000000
     ptrs = [P + i * 0x100000 for i in range(9)]
-    args = ptrs + [B, H, 2, N, d, bwd_st, 1, 0.125, ws, lib.fa_bwd_workspace_bytes(B, H, N, d), None]
+    args = ptrs + [B, H, 2, N, d, bwd_st, 1, 0.125, ws, lib.fa_bwd_strided_workspace_bytes(B, H, 2, N, d, 1), None]
     bad = list(args)
     bad[14] = None
     assert lib.fa_bwd_strided(*bad) == 1
@@ -151,6 +167,9 @@ def test_strided_entry_points_reject_bad_arguments():
     assert lib.fa_bwd_strided(*bad) == 7
     bad = list(args)
     bad[17] = ws + 8                                        # misaligned workspace
+    assert lib.fa_bwd_strided(*bad) == 5
+    bad = list(args)
+    bad[18] = lib.fa_bwd_workspace_bytes(B, H, N, d)        # no room for the partials
     assert lib.fa_bwd_strided(*bad) == 5
 
 

@@ -105,3 +105,36 @@ def test_gqa_n2048_d128_causal(gpu):
     ro, rl = A.forward_gqa(x["q"], x["k"], x["v"], True, scale)
     _check_fwd(o, lse, ro, rl, "gqa n2048")
     _check_grads((dq, dk, dv), A.backward_gqa(x["q"], x["k"], x["v"], x["do"], True, scale), "gqa n2048")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_n8192_d128_sampled(gpu, causal):
+    """H=16 query heads on H_kv=2 at N=8192 (the work of one K/V head's key
+    block is then shared by several workgroups, whose fp32 partials a
+    reduction adds): sampled dQ rows of two query heads and dK / dV rows of
+    both K/V heads, each summed over its 8 query heads."""
+    B, H, Hkv, N, d = 1, 16, 2, 8192, 128
+    x = fa_inputs.grouped_inputs(B, H, Hkv, N, d, seed=3200 + causal, with_do=True)
+    q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = gpu.fwd(q, k, v, causal=causal)
+    dq, dk, dv = (to_host(t) for t in gpu.bwd(q, k, v, o, do, lse, causal=causal))
+    idx = np.unique(np.concatenate([[0, 1, 127, 128, 4095, 8190, 8191],
+                                    np.random.default_rng(7).integers(0, N, 12)]))
+    g = H // Hkv
+    for h in (0, 13):
+        hk = h // g
+        rq = A.backward_head_rows(x["q"][0, h], x["k"][0, hk], x["v"][0, hk], x["do"][0, h], idx, causal, scale)
+        e = A.rel_rms(dq[0, h, idx], rq)
+        print("c%d dQ head %d rel_rms=%.3e" % (causal, h, e), flush=True)
+        assert e <= GRAD_REL_RMS
+    for hk in range(Hkv):
+        rk = np.zeros((len(idx), d))
+        rv = np.zeros((len(idx), d))
+        for h in range(hk * g, (hk + 1) * g):
+            a, c = A.backward_head_cols(x["q"][0, h], x["k"][0, hk], x["v"][0, hk], x["do"][0, h], idx, causal, scale)
+            rk += a
+            rv += c
+        ek, ev = A.rel_rms(dk[0, hk, idx], rk), A.rel_rms(dv[0, hk, idx], rv)
+        print("c%d dK/dV kv head %d rel_rms=%.3e %.3e" % (causal, hk, ek, ev), flush=True)
+        assert ek <= GRAD_REL_RMS and ev <= GRAD_REL_RMS

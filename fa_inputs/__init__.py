@@ -72,6 +72,11 @@ def grouped_inputs(B: int, H: int, H_kv: int, N: int, d: int, seed: int, with_do
     return {n: to_bf16_values(rng.standard_normal((B, heads[n], N, d), dtype=np.float32)) for n in names}
 
 
+def alibi_slopes(H: int) -> np.ndarray:
+    """float32 [H] ALiBi slopes on the usual geometric schedule 2^(-8 (h + 1) / H)."""
+    return (2.0 ** (-8.0 * (np.arange(H) + 1) / H)).astype(np.float32)
+
+
 def hadamard_signs(seed: int = HADAMARD_SEED) -> np.ndarray:
     """128 random signs (int8, +-1)."""
     rng = np.random.Generator(np.random.PCG64(seed))

@@ -171,6 +171,147 @@ def backward_gqa(q, k, v, do, causal: bool = False, scale: float | None = None):
     return dq, dk.reshape(B, Hkv, g, N, d).sum(axis=2), dv.reshape(B, Hkv, g, N, d).sum(axis=2)
 
 
+# ------------------------------------------- masks, ALiBi, cross-attention
+# [LIB] "Cases where FlashAttention does not help" lists the masks and shapes
+# the kernels ship beyond causal: sliding windows, ALiBi, cross-attention
+# (query and key lengths differ). The pages name them without formulas; the
+# readings used here are:
+# * diagonal: query i (of N_q) is aligned with key i + N_k - N_q (bottom-right
+#   alignment: the last query sits on the last key; N_q = N_k gives i);
+# * causal: keys after the diagonal are hidden;
+# * window (left, right): only keys within [diagonal - left, diagonal + right]
+#   are visible; -1 leaves that side unbounded;
+# * ALiBi: the scaled score gets the bias -slope_h * |diagonal - j|, one slope
+#   per query head;
+# * a query that sees no key at all (possible only with N_q > N_k or a window
+#   clear of the keys) has O = 0 and LSE = -inf (log of an empty sum).
+
+def visible(n_q: int, n_k: int, causal: bool, window=(-1, -1)) -> np.ndarray:
+    """Boolean [n_q, n_k]: True where query i may attend to key j."""
+    diag = np.arange(n_q)[:, None] + (n_k - n_q)
+    j = np.arange(n_k)[None, :]
+    vis = np.ones((n_q, n_k), dtype=bool)
+    left, right = window
+    if causal:
+        vis &= j <= diag
+    if left >= 0:
+        vis &= j >= diag - left
+    if right >= 0:
+        vis &= j <= diag + right
+    return vis
+
+
+def alibi_bias(n_q: int, n_k: int, slope: float) -> np.ndarray:
+    """[n_q, n_k] bias -slope |i + n_k - n_q - j| (slope as its float32 value)."""
+    diag = np.arange(n_q)[:, None] + (n_k - n_q)
+    return -float(np.float32(slope)) * np.abs(diag - np.arange(n_k)[None, :]).astype(np.float64)
+
+
+def general_scores(q, k, scale: float, causal: bool, window=(-1, -1), slope=None, rows=None):
+    """S = s Q K^T (+ ALiBi bias) for one head, hidden entries -inf."""
+    q = _f64(q)
+    k = _f64(k)
+    n_q, n_k = q.shape[0], k.shape[0]
+    idx = np.arange(n_q) if rows is None else np.asarray(rows)
+    s = scale_as_f32(scale) * (q[idx] @ k.T)
+    if slope is not None:
+        s = s + alibi_bias(n_q, n_k, slope)[idx]
+    s[~visible(n_q, n_k, causal, window)[idx]] = -np.inf
+    return s
+
+
+def softmax_rows_or_empty(s: np.ndarray):
+    """Safe softmax per row; a row with no finite score gives P = 0, LSE = -inf."""
+    empty = np.isneginf(s).all(axis=1)
+    m = np.where(empty, 0.0, s.max(axis=1))
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    p = e / np.where(empty, 1.0, l)[:, None]
+    lse = np.where(empty, -np.inf, m + np.log(np.where(empty, 1.0, l)))
+    return p, lse
+
+
+def _kv_head(h: int, H: int, Hkv: int) -> int:
+    return h // (H // Hkv)
+
+
+def forward_general(q, k, v, causal: bool = False, scale: float | None = None, window=(-1, -1),
+                    slopes=None):
+    """(O, LSE) for q [B, H, N_q, d], k, v [B, H_kv, N_k, d] with the masks above;
+    ``slopes`` is None or H ALiBi slopes."""
+    q, k, v = (_f64(x) for x in (q, k, v))
+    B, H, n_q, d = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = default_scale(d)
+    o = np.empty((B, H, n_q, v.shape[-1]))
+    lse = np.empty((B, H, n_q))
+    for b in range(B):
+        for h in range(H):
+            hk = _kv_head(h, H, Hkv)
+            sl = None if slopes is None else slopes[h]
+            p, lse[b, h] = softmax_rows_or_empty(general_scores(q[b, h], k[b, hk], scale, causal, window, sl))
+            o[b, h] = p @ v[b, hk]
+    return o, lse
+
+
+def backward_general(q, k, v, do, causal: bool = False, scale: float | None = None, window=(-1, -1),
+                     slopes=None):
+    """(dQ, dK, dV) for forward_general (slopes are constants, not differentiated);
+    dK, dV of a shared key/value head summed over its query heads."""
+    q, k, v, do = (_f64(x) for x in (q, k, v, do))
+    B, H, n_q, d = q.shape
+    Hkv = k.shape[1]
+    if scale is None:
+        scale = default_scale(d)
+    s = scale_as_f32(scale)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            hk = _kv_head(h, H, Hkv)
+            sl = None if slopes is None else slopes[h]
+            p, _ = softmax_rows_or_empty(general_scores(q[b, h], k[b, hk], scale, causal, window, sl))
+            dv[b, hk] += p.T @ do[b, h]
+            dp = do[b, h] @ v[b, hk].T
+            dd = (p * dp).sum(axis=1)
+            ds = p * (dp - dd[:, None])
+            dq[b, h] = s * (ds @ k[b, hk])
+            dk[b, hk] += s * (ds.T @ q[b, h])
+    return dq, dk, dv
+
+
+def general_head_rows(q, k, v, do, rows, causal: bool, scale: float, window=(-1, -1), slope=None):
+    """O, LSE and dQ of the selected query rows of one head (general masks)."""
+    q, k, v, do = (_f64(x) for x in (q, k, v, do))
+    rows = np.asarray(rows)
+    p, lse = softmax_rows_or_empty(general_scores(q, k, scale, causal, window, slope, rows))
+    dp = do[rows] @ v.T
+    dd = (p * dp).sum(axis=1)
+    ds = p * (dp - dd[:, None])
+    return p @ v, lse, scale_as_f32(scale) * (ds @ k)
+
+
+def general_head_cols(q, k, v, do, cols, causal: bool, scale: float, window=(-1, -1), slope=None,
+                      chunk: int = 1024):
+    """(dK, dV) of the selected key rows of one (query head, key/value head) pair."""
+    q, k, v, do = (_f64(x) for x in (q, k, v, do))
+    cols = np.asarray(cols)
+    n = q.shape[0]
+    dk = np.zeros((cols.size, q.shape[1]))
+    dv = np.zeros((cols.size, v.shape[1]))
+    for r0 in range(0, n, chunk):
+        rows = np.arange(r0, min(n, r0 + chunk))
+        p, _ = softmax_rows_or_empty(general_scores(q, k, scale, causal, window, slope, rows))
+        dp = do[rows] @ v.T
+        dd = (p * dp).sum(axis=1)
+        ds_cols = p[:, cols] * (dp[:, cols] - dd[:, None])
+        dv += p[:, cols].T @ do[rows]
+        dk += scale_as_f32(scale) * (ds_cols.T @ q[rows])
+    return dk, dv
+
+
 def row_delta(o, do):
     """D_i = sum_k dO_ik O_ik (equal to sum_j P_ij dP_ij because O = P V)."""
     return (_f64(o) * _f64(do)).sum(axis=-1)

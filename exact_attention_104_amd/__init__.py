@@ -8,7 +8,9 @@ raises.
     o, lse = fwd(q, k, v, causal=True)                  # bf16 [B, H, N, d] CUDA tensors
     dq, dk, dv = bwd(q, k, v, o, do, lse, causal=True)
     # any [B, H, N, d] views with contiguous d (e.g. [B, N, H, d].transpose(1, 2)),
-    # and grouped K/V heads: k, v of shape [B, H_kv, N, d] with H_kv dividing H
+    # and grouped K/V heads: k, v of shape [B, H_kv, N, d] with H_kv dividing H;
+    # k, v may have another length N_k (cross-attention), and
+    o, lse = fwd(q, k, v, causal=True, window=(256, 0), alibi_slopes=slopes)  # slopes: fp32 [H]
     q8, qs = quant_fp8(q, signs)                        # signs: int8 [128] or None
     o8, lse8 = fwd_fp8(q8, k8, v8, qs, ks, vs, causal=True)
 """
@@ -39,6 +41,12 @@ class Strides(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("head", ctypes.c_int64), ("row", ctypes.c_int64)]
 
 
+class Mask(ctypes.Structure):
+    """fa_mask: causal flag, sliding window (left, right; -1 unbounded), ALiBi slopes."""
+    _fields_ = [("causal", ctypes.c_int), ("window_left", ctypes.c_int), ("window_right", ctypes.c_int),
+                ("alibi_slopes", ctypes.c_void_p)]
+
+
 # exported symbol -> (restype, argtypes)
 SIGNATURES = {
     "fa_status_string": (ctypes.c_char_p, [_I]),
@@ -49,6 +57,9 @@ SIGNATURES = {
     "fa_bwd": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _F, _P, ctypes.c_size_t, _P]),
     "fa_bwd_strided": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _P, _I, _F, _P, ctypes.c_size_t, _P]),
     "fa_bwd_strided_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
+    "fa_fwd_ext": (_I, [_P] * 5 + [_I] * 6 + [_P, _P, _F, _P]),
+    "fa_bwd_ext_workspace_bytes": (ctypes.c_size_t, [_I] * 6 + [_P]),
+    "fa_bwd_ext": (_I, [_P] * 9 + [_I] * 6 + [_P, _P, _F, _P, ctypes.c_size_t, _P]),
     "fa_quant_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_fwd_fp8": (_I, [_P] * 8 + [_I, _I, _I, _I, _I, _F, _P]),
 }
@@ -147,64 +158,96 @@ def _raise(st, call):
         raise FAError(st, call)
 
 
-def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """bf16 forward: returns (O bf16 [B,H,N,d], LSE fp32 [B,H,N]).
+def _mask(causal, window, alibi_slopes, H, device):
+    """fa_mask for the arguments, or None when the plain calls suffice."""
+    left, right = (int(window[0]), int(window[1])) if window is not None else (-1, -1)
+    if alibi_slopes is not None:
+        _check_tensor("alibi_slopes", alibi_slopes, torch.float32, (H,))
+        if alibi_slopes.device != device:
+            raise ValueError("alibi_slopes must be on the device of q")
+    if (left, right) == (-1, -1) and alibi_slopes is None:
+        return None
+    return Mask(int(bool(causal)), left, right, alibi_slopes.data_ptr() if alibi_slopes is not None else None)
 
-    q: [B, H, N, d]; k, v: [B, H_kv, N, d] (H_kv divides H: grouped / multi-query
-    heads); any views with a contiguous last dimension. O takes q's layout."""
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, window=None,
+        alibi_slopes=None):
+    """bf16 forward: returns (O bf16 [B,H,N_q,d], LSE fp32 [B,H,N_q]).
+
+    q: [B, H, N_q, d]; k, v: [B, H_kv, N_k, d] (H_kv divides H: grouped / multi-query
+    heads; N_k != N_q: cross-attention, the last query aligned with the last key);
+    any views with a contiguous last dimension. window = (left, right) keys around
+    each query's diagonal key (-1: unbounded); alibi_slopes: fp32 [H] on the GPU.
+    O takes q's layout."""
     lib = load_library()
-    B, H, Hkv, N, d = _kv_heads(q, k, v)
-    _check_view("q", q, (B, H, N, d))
-    _check_view("k", k, (B, Hkv, N, d))
-    _check_view("v", v, (B, Hkv, N, d))
+    B, H, Hkv, Nq, d = _kv_heads(q, k, v)
+    Nk = int(k.shape[2])
+    _check_view("q", q, (B, H, Nq, d))
+    _check_view("k", k, (B, Hkv, Nk, d))
+    _check_view("v", v, (B, Hkv, Nk, d))
     o = torch.empty_like(q) if out is None else out
-    lse_t = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check_view("out", o, (B, H, N, d))
-    _check_tensor("lse", lse_t, torch.float32, (B, H, N))
+    lse_t = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_view("out", o, (B, H, Nq, d))
+    _check_tensor("lse", lse_t, torch.float32, (B, H, Nq))
     sc, c = _scale(scale, d), int(bool(causal))
-    if Hkv == H and all(t.is_contiguous() for t in (q, k, v, o)):
-        st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
-                        B, H, N, d, c, sc, _stream())
+    m = _mask(causal, window, alibi_slopes, H, q.device)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr())
+    if m is not None or Nk != Nq:
+        m = m if m is not None else Mask(c, -1, -1, None)
+        st = lib.fa_fwd_ext(*ptrs, B, H, Hkv, Nq, Nk, d, _strides(q, k, v, o), ctypes.byref(m), sc, _stream())
+        _raise(st, "fa_fwd_ext")
+    elif Hkv == H and all(t.is_contiguous() for t in (q, k, v, o)):
+        st = lib.fa_fwd(*ptrs, B, H, Nq, d, c, sc, _stream())
         _raise(st, "fa_fwd")
     else:
-        st = lib.fa_fwd_strided(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_t.data_ptr(),
-                                B, H, Hkv, N, d, _strides(q, k, v, o), c, sc, _stream())
+        st = lib.fa_fwd_strided(*ptrs, B, H, Hkv, Nq, d, _strides(q, k, v, o), c, sc, _stream())
         _raise(st, "fa_fwd_strided")
     return o, lse_t
 
 
-def bwd_workspace_bytes(B, H, N, d, H_kv=None, causal=False) -> int:
-    """Workspace bytes of bwd: fa_bwd's, or with H_kv key/value heads fa_bwd_strided's."""
+def bwd_workspace_bytes(B, H, N, d, H_kv=None, causal=False, N_k=None, window=None, alibi=False) -> int:
+    """Workspace bytes of bwd: fa_bwd's, or (H_kv, N_k or a window given) fa_bwd_ext's."""
     lib = load_library()
-    if H_kv is None:
+    if H_kv is None and N_k is None and window is None:
         return int(lib.fa_bwd_workspace_bytes(B, H, N, d))
-    return int(lib.fa_bwd_strided_workspace_bytes(B, H, H_kv, N, d, int(bool(causal))))
+    left, right = window if window is not None else (-1, -1)
+    m = Mask(int(bool(causal)), int(left), int(right), None)
+    return int(lib.fa_bwd_ext_workspace_bytes(B, H, H if H_kv is None else H_kv, N, N if N_k is None else N_k,
+                                              d, ctypes.byref(m)))
 
 
-def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, workspace=None):
+def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, workspace=None, window=None,
+        alibi_slopes=None):
     """bf16 backward by recomputation: returns (dQ, dK, dV) bf16.
 
-    Shapes and layouts as in fwd; dK, dV have k's and v's shapes and layouts
-    (for grouped heads, the sums over each group's query heads)."""
+    Shapes, layouts and masks as in fwd; dK, dV have k's and v's shapes and
+    layouts (for grouped heads, the sums over each group's query heads)."""
     lib = load_library()
-    B, H, Hkv, N, d = _kv_heads(q, k, v)
+    B, H, Hkv, Nq, d = _kv_heads(q, k, v)
+    Nk = int(k.shape[2])
     for n, t in (("q", q), ("o", o), ("do", do)):
-        _check_view(n, t, (B, H, N, d))
+        _check_view(n, t, (B, H, Nq, d))
     for n, t in (("k", k), ("v", v)):
-        _check_view(n, t, (B, Hkv, N, d))
-    _check_tensor("lse", lse, torch.float32, (B, H, N))
+        _check_view(n, t, (B, Hkv, Nk, d))
+    _check_tensor("lse", lse, torch.float32, (B, H, Nq))
     sc, c = _scale(scale, d), int(bool(causal))
-    need = int(lib.fa_bwd_strided_workspace_bytes(B, H, Hkv, N, d, c))
+    m = _mask(causal, window, alibi_slopes, H, q.device)
+    mm = m if m is not None else Mask(c, -1, -1, None)
+    need = int(lib.fa_bwd_ext_workspace_bytes(B, H, Hkv, Nq, Nk, d, ctypes.byref(mm)))
     ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
     _check_tensor("workspace", ws, torch.uint8)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
-    if Hkv == H and all(t.is_contiguous() for t in (q, k, v, o, do, dq, dk, dv)):
-        st = lib.fa_bwd(*ptrs, B, H, N, d, c, sc, ws.data_ptr(), ws.numel(), _stream())
+    if m is not None or Nk != Nq:
+        st = lib.fa_bwd_ext(*ptrs, B, H, Hkv, Nq, Nk, d, _strides(q, k, v, o, do, dq, dk, dv), ctypes.byref(mm),
+                            sc, ws.data_ptr(), ws.numel(), _stream())
+        _raise(st, "fa_bwd_ext")
+    elif Hkv == H and all(t.is_contiguous() for t in (q, k, v, o, do, dq, dk, dv)):
+        st = lib.fa_bwd(*ptrs, B, H, Nq, d, c, sc, ws.data_ptr(), ws.numel(), _stream())
         _raise(st, "fa_bwd")
     else:
-        st = lib.fa_bwd_strided(*ptrs, B, H, Hkv, N, d, _strides(q, k, v, o, do, dq, dk, dv), c, sc,
+        st = lib.fa_bwd_strided(*ptrs, B, H, Hkv, Nq, d, _strides(q, k, v, o, do, dq, dk, dv), c, sc,
                                 ws.data_ptr(), ws.numel(), _stream())
         _raise(st, "fa_bwd_strided")
     return dq, dk, dv

@@ -4,6 +4,7 @@
 // a launch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -59,6 +60,33 @@ bool scalars_ok(int causal, float scale) {
   return (causal == 0 || causal == 1) && std::isfinite(scale) && scale > 0.f;
 }
 
+bool scale_ok(float scale) { return std::isfinite(scale) && scale > 0.f; }
+
+constexpr int kMaxLen = 1 << 24;
+
+// A mask is valid with causal 0 / 1 and each window side -1 (unbounded) or
+// 0 .. 2^24; NULL means no mask.
+bool mask_ok(const fa_mask* m) {
+  if (!m) return true;
+  return (m->causal == 0 || m->causal == 1) && m->window_left >= -1 && m->window_left <= kMaxLen &&
+         m->window_right >= -1 && m->window_right <= kMaxLen;
+}
+
+// The band of visible keys (fa_internal.h) for a mask and the two lengths.
+fa::Band band_of(const fa_mask* m, int N_q, int N_k) {
+  fa::Band b{N_k - N_q, fa::kOpen, fa::kOpen};
+  if (!m) return b;
+  if (m->window_left >= 0) b.wl = m->window_left;
+  if (m->window_right >= 0) b.wr = m->window_right;
+  if (m->causal) b.wr = std::min(b.wr, 0);
+  return b;
+}
+
+// Work per key block is uneven when the band is bounded on either side.
+bool uneven(const fa_mask* m) {
+  return m && (m->causal || m->window_left >= 0 || m->window_right >= 0);
+}
+
 // A [B, Hx, N, d] view with element strides st and contiguous d.
 struct View {
   const void* p;
@@ -111,34 +139,44 @@ const char* fa_status_string(int status) {
     case FA_ERR_DEVICE: return "FA_ERR_DEVICE: no gfx950 device current";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps another tensor";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
-    case FA_ERR_ARG: return "FA_ERR_ARG: causal must be 0/1 and scale finite and positive";
+    case FA_ERR_ARG: return "FA_ERR_ARG: bad causal flag, window, scale or stride";
     default: return "FA_ERR_UNKNOWN";
   }
 }
 
 int fa_abi_version(void) { return FA_ABI_VERSION; }
 
+int fa_fwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+               int B, int H, int H_kv, int N_q, int N_k, int d, const fa_strides* st, const fa_mask* mask,
+               float scale, void* stream) {
+  if (!scale_ok(scale) || !mask_ok(mask)) return FA_ERR_ARG;
+  if (!q || !k || !v || !o || !lse || !st) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!shape_ok(B, H, N_q, d) || !shape_ok(B, H_kv, N_k, d) || H_kv < 1 || H % H_kv != 0) return FA_ERR_SHAPE;
+  const View vq{q, B, H, N_q, d, st[0]}, vk{k, B, H_kv, N_k, d, st[1]}, vv{v, B, H_kv, N_k, d, st[2]},
+      vo{o, B, H, N_q, d, st[3]};
+  if (!vq.strides_ok() || !vk.strides_ok() || !vv.strides_ok() || !vo.strides_ok()) return FA_ERR_ARG;
+  const float* slopes = mask ? mask->alibi_slopes : nullptr;
+  if (!vq.aligned() || !vk.aligned() || !vv.aligned() || !vo.aligned() || !aligned16(lse) ||
+      ((uintptr_t)slopes & 3u))
+    return FA_ERR_ALIGN;
+  const size_t lb = (size_t)B * H * N_q * 4;
+  const Range ins[4] = {vq.range(), vk.range(), vv.range(), span(slopes, slopes ? (size_t)H * 4 : 0)};
+  const Range outs[2] = {vo.range(), span(lse, lb)};
+  if (!vo.injective() || any_alias(outs, 2, ins, 4)) return FA_ERR_ALIAS;
+  if (int s = check_device()) return s;
+  auto S = [&](int i) { return fa::Strides{st[i].batch, st[i].head, st[i].row}; };
+  fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, band_of(mask, N_q, N_k), slopes, scale,
+                S(0), S(1), S(2), S(3), stream};
+  return fa::launch_fwd(a) ? FA_ERR_LAUNCH : FA_OK;
+}
+
 int fa_fwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                    int B, int H, int H_kv, int N, int d, const fa_strides* st, int causal, float scale,
                    void* stream) {
-  if (!scalars_ok(causal, scale)) return FA_ERR_ARG;
-  if (!q || !k || !v || !o || !lse || !st) return FA_ERR_NULL;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (!shape_ok(B, H, N, d) || H_kv < 1 || H % H_kv != 0) return FA_ERR_SHAPE;
-  const View vq{q, B, H, N, d, st[0]}, vk{k, B, H_kv, N, d, st[1]}, vv{v, B, H_kv, N, d, st[2]},
-      vo{o, B, H, N, d, st[3]};
-  if (!vq.strides_ok() || !vk.strides_ok() || !vv.strides_ok() || !vo.strides_ok()) return FA_ERR_ARG;
-  if (!vq.aligned() || !vk.aligned() || !vv.aligned() || !vo.aligned() || !aligned16(lse)) return FA_ERR_ALIGN;
-  const size_t lb = (size_t)B * H * N * 4;
-  const Range ins[3] = {vq.range(), vk.range(), vv.range()};
-  const Range outs[2] = {vo.range(), span(lse, lb)};
-  if (!vo.injective() || any_alias(outs, 2, ins, 3)) return FA_ERR_ALIAS;
-  if (int s = check_device()) return s;
-  fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N, d, causal, scale,
-                fa::Strides{st[0].batch, st[0].head, st[0].row}, fa::Strides{st[1].batch, st[1].head, st[1].row},
-                fa::Strides{st[2].batch, st[2].head, st[2].row}, fa::Strides{st[3].batch, st[3].head, st[3].row},
-                stream};
-  return fa::launch_fwd(a) ? FA_ERR_LAUNCH : FA_OK;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  const fa_mask m{causal, -1, -1, nullptr};
+  return fa_fwd_ext(q, k, v, o, lse, B, H, H_kv, N, N, d, st, &m, scale, stream);
 }
 
 int fa_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
@@ -153,43 +191,61 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
   return fa::bwd_delta_bytes(B, H, N);
 }
 
+size_t fa_bwd_ext_workspace_bytes(int B, int H, int H_kv, int N_q, int N_k, int d, const fa_mask* mask) {
+  if ((d != 64 && d != 128) || !shape_ok(B, H, N_q, d) || !shape_ok(B, H_kv, N_k, d) || H_kv < 1 ||
+      H % H_kv != 0 || !mask_ok(mask))
+    return 0;
+  const int split = fa::bwd_kv_split(B, H_kv, H / H_kv, N_k, uneven(mask));
+  return fa::bwd_delta_bytes(B, H, N_q) + fa::bwd_partial_bytes(B, H_kv, N_k, d, split);
+}
+
 size_t fa_bwd_strided_workspace_bytes(int B, int H, int H_kv, int N, int d, int causal) {
-  if ((d != 64 && d != 128) || !shape_ok(B, H, N, d) || H_kv < 1 || H % H_kv != 0) return 0;
   if (causal != 0 && causal != 1) return 0;
-  const int split = fa::bwd_kv_split(B, H_kv, H / H_kv, N, causal);
-  return fa::bwd_delta_bytes(B, H, N) + fa::bwd_partial_bytes(B, H_kv, N, d, split);
+  const fa_mask m{causal, -1, -1, nullptr};
+  return fa_bwd_ext_workspace_bytes(B, H, H_kv, N, N, d, &m);
+}
+
+int fa_bwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+               const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+               int B, int H, int H_kv, int N_q, int N_k, int d, const fa_strides* st, const fa_mask* mask,
+               float scale, void* ws, size_t ws_bytes, void* stream) {
+  if (!scale_ok(scale) || !mask_ok(mask)) return FA_ERR_ARG;
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !st) return FA_ERR_NULL;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!shape_ok(B, H, N_q, d) || !shape_ok(B, H_kv, N_k, d) || H_kv < 1 || H % H_kv != 0) return FA_ERR_SHAPE;
+  const View vq{q, B, H, N_q, d, st[0]}, vk{k, B, H_kv, N_k, d, st[1]}, vv{v, B, H_kv, N_k, d, st[2]},
+      vo{o, B, H, N_q, d, st[3]}, vdo{dO, B, H, N_q, d, st[4]}, vdq{dq, B, H, N_q, d, st[5]},
+      vdk{dk, B, H_kv, N_k, d, st[6]}, vdv{dv, B, H_kv, N_k, d, st[7]};
+  const View* all[8] = {&vq, &vk, &vv, &vo, &vdo, &vdq, &vdk, &vdv};
+  for (const View* x : all)
+    if (!x->strides_ok()) return FA_ERR_ARG;
+  for (const View* x : all)
+    if (!x->aligned()) return FA_ERR_ALIGN;
+  const float* slopes = mask ? mask->alibi_slopes : nullptr;
+  if (!aligned16(lse) || ((uintptr_t)slopes & 3u)) return FA_ERR_ALIGN;
+  const size_t need = fa_bwd_ext_workspace_bytes(B, H, H_kv, N_q, N_k, d, mask);
+  if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need) return FA_ERR_WORKSPACE;
+  const size_t lb = (size_t)B * H * N_q * 4;
+  const Range ins[7] = {vq.range(), vk.range(), vv.range(), vo.range(), vdo.range(), span(lse, lb),
+                        span(slopes, slopes ? (size_t)H * 4 : 0)};
+  const Range outs[4] = {vdq.range(), vdk.range(), vdv.range(), span(ws, need)};
+  if (!vdq.injective() || !vdk.injective() || !vdv.injective() || any_alias(outs, 4, ins, 7)) return FA_ERR_ALIAS;
+  if (int s = check_device()) return s;
+  auto S = [&](int i) { return fa::Strides{st[i].batch, st[i].head, st[i].row}; };
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, (float*)ws, B, H, H_kv, N_q, N_k, d,
+                band_of(mask, N_q, N_k), slopes, scale, S(0), S(1), S(2), S(3), S(4), S(5), S(6), S(7), stream};
+  a.split = fa::bwd_kv_split(B, H_kv, H / H_kv, N_k, uneven(mask));
+  a.part = a.split > 1 ? (float*)((char*)ws + fa::bwd_delta_bytes(B, H, N_q)) : nullptr;
+  return fa::launch_bwd(a) ? FA_ERR_LAUNCH : FA_OK;
 }
 
 int fa_bwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
                    const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                    int B, int H, int H_kv, int N, int d, const fa_strides* st, int causal, float scale,
                    void* ws, size_t ws_bytes, void* stream) {
-  if (!scalars_ok(causal, scale)) return FA_ERR_ARG;
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !st) return FA_ERR_NULL;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (!shape_ok(B, H, N, d) || H_kv < 1 || H % H_kv != 0) return FA_ERR_SHAPE;
-  const View vq{q, B, H, N, d, st[0]}, vk{k, B, H_kv, N, d, st[1]}, vv{v, B, H_kv, N, d, st[2]},
-      vo{o, B, H, N, d, st[3]}, vdo{dO, B, H, N, d, st[4]}, vdq{dq, B, H, N, d, st[5]},
-      vdk{dk, B, H_kv, N, d, st[6]}, vdv{dv, B, H_kv, N, d, st[7]};
-  const View* all[8] = {&vq, &vk, &vv, &vo, &vdo, &vdq, &vdk, &vdv};
-  for (const View* x : all)
-    if (!x->strides_ok()) return FA_ERR_ARG;
-  for (const View* x : all)
-    if (!x->aligned()) return FA_ERR_ALIGN;
-  if (!aligned16(lse)) return FA_ERR_ALIGN;
-  const size_t need = fa_bwd_strided_workspace_bytes(B, H, H_kv, N, d, causal);
-  if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need) return FA_ERR_WORKSPACE;
-  const size_t lb = (size_t)B * H * N * 4;
-  const Range ins[6] = {vq.range(), vk.range(), vv.range(), vo.range(), vdo.range(), span(lse, lb)};
-  const Range outs[4] = {vdq.range(), vdk.range(), vdv.range(), span(ws, need)};
-  if (!vdq.injective() || !vdk.injective() || !vdv.injective() || any_alias(outs, 4, ins, 6)) return FA_ERR_ALIAS;
-  if (int s = check_device()) return s;
-  auto S = [&](int i) { return fa::Strides{st[i].batch, st[i].head, st[i].row}; };
-  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, (float*)ws, B, H, H_kv, N, d, causal, scale,
-                S(0), S(1), S(2), S(3), S(4), S(5), S(6), S(7), stream};
-  a.split = fa::bwd_kv_split(B, H_kv, H / H_kv, N, causal);
-  a.part = a.split > 1 ? (float*)((char*)ws + fa::bwd_delta_bytes(B, H, N)) : nullptr;
-  return fa::launch_bwd(a) ? FA_ERR_LAUNCH : FA_OK;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  const fa_mask m{causal, -1, -1, nullptr};
+  return fa_bwd_ext(q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, N, N, d, st, &m, scale, ws, ws_bytes, stream);
 }
 
 int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,

@@ -67,16 +67,25 @@ pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, floa
 // ---------------------------------------------------------------------------
 // dK, dV: key-stationary
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+// Masks as in the forward: query i sees keys i + off - wl .. i + off + wr of
+// 0 .. Nk - 1; a key block visits only the query blocks whose band reaches it,
+// and masks only steps that cut the band's edges. kMaskBandAlibi adds
+// -slope_h |i + off - j| to the scaled scores; kMaskNone keeps the fixed
+// arithmetic. (Causal runs as a band here: a causal-only instance compiled to
+// a worse register allocation.)
+template <int D, int MASK>
 __global__ void __launch_bounds__(256, 1)
 dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
             const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
             uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, float* __restrict__ part, int BHkv, int H,
-            int group, int split, int N, int nkb, float scale, float scale_log2, Strides sq, Strides sk,
-            Strides sv, Strides sdo, Strides sdk, Strides sdv) {
+            int group, int split, int Nq, int Nk, int nkb, float scale, float scale_log2, Band band,
+            const float* __restrict__ slopes, Strides sq, Strides sk, Strides sv, Strides sdo, Strides sdk,
+            Strides sdv) {
   constexpr int KS = D / 16;    // k-steps over d
   constexpr int DB = D / 32;    // 32-wide d blocks
   constexpr int QT = kBQ * D;   // elements of a Q or dO tile
+  static_assert(MASK != kMaskCausal, "causal runs as a band");
+  constexpr bool BAND = MASK >= kMaskBand, ALIBI = MASK == kMaskBandAlibi;
 
   // Three buffers: while step j's dV / dK products read buffer j % 3 and step
   // j+1's S / dP products read buffer (j+1) % 3, step j+2 loads into the third.
@@ -110,14 +119,43 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
   const int kw0 = kb0 + w * 32;
   const int key_l = kw0 + (lane & 31);  // this lane's key in S / dP
 
-  // Steps run over the query heads h0 .. h0 + gs - 1 in turn; within a head, from the last query block down (so that the
-  // concurrent key blocks of a head read the same Q / dO tiles at about the
-  // same time) to block qs_lo (causal: blocks below the key block are all
-  // masked).
-  const int nqs = (N + kBQ - 1) / kBQ;
-  const int qs_lo = CAUSAL ? kb0 / kBQ : 0;
-  const int nsteps = (nqs - qs_lo) * gs;
-  const int q_hi = (nqs - 1) * kBQ, q_lo = qs_lo * kBQ;
+  // Steps run over the query heads h0 .. h0 + gs - 1 in turn; within a head,
+  // over the query blocks whose band reaches this key block, from the last
+  // down (so that the concurrent key blocks of a head read the same Q / dO
+  // tiles at about the same time).
+  int qs_lo, nsq;  // first query block, query blocks per head
+  if constexpr (BAND) {
+    const int kblast = min(kb0 + kBKC, Nk) - 1;
+    const int qa = max(0, kb0 - band.off - band.wr);          // first query seeing a key of the block
+    const int qz = min(Nq - 1, kblast - band.off + band.wl);  // last such query
+    qs_lo = qa / kBQ;
+    nsq = qz >= qa ? qz / kBQ - qs_lo + 1 : 0;
+  } else {
+    qs_lo = 0;
+    nsq = (Nq + kBQ - 1) / kBQ;
+  }
+  const int nsteps = nsq * gs;
+  const int q_hi = (qs_lo + nsq - 1) * kBQ, q_lo = qs_lo * kBQ;
+
+  if (BAND && nsteps == 0) {  // no query sees these keys: dK = dV = 0
+    constexpr int CH = D / 8;
+    for (int e = tid; e < kBKC * CH; e += 256) {
+      const int key = kb0 + e / CH, c = (e % CH) * 8;
+      if (key >= Nk) continue;
+      if (split == 1) {
+        *(u32x4*)(dKg + b * sdk.b + hk * sdk.h + (size_t)key * sdk.n + c) = u32x4{0, 0, 0, 0};
+        *(u32x4*)(dVg + b * sdv.b + hk * sdv.h + (size_t)key * sdv.n + c) = u32x4{0, 0, 0, 0};
+      } else {
+        float* pk = part + ((size_t)unit * Nk + key) * D + c;
+        float* pv = pk + (size_t)BHkv * split * Nk * D;
+        *(f32x4*)pk = f32x4{0.f, 0.f, 0.f, 0.f};
+        *(f32x4*)(pk + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+        *(f32x4*)pv = f32x4{0.f, 0.f, 0.f, 0.f};
+        *(f32x4*)(pv + 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    return;
+  }
   // query block after q0 in step order (wrapping to the next head's last)
   auto next_q0 = [&](int q0) { return q0 == q_lo ? q_hi : q0 - kBQ; };
   // Buffer j % 3 of the three (chosen at run time: one set of lane offsets
@@ -130,23 +168,36 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
   int ld_q0 = q_hi;
   const uint16_t* ld_q = Qg + b * sq.b + (long long)h0 * sq.h;
   const uint16_t* ld_o = dOg + b * sdo.b + (long long)h0 * sdo.h;
-  size_t ld_row = ((size_t)b * H + h0) * N;  // LSE / D row of the head
+  size_t ld_row = ((size_t)b * H + h0) * Nq;  // LSE / D row of the head
   auto issue_loads = [&](int j) __attribute__((always_inline)) {
-    load_tile_async<D, kBQ, 256, true>(bufQ(j), ld_q, sq.n, ld_q0, N, tid);
-    load_tile_async<D, kBQ, 256, true>(bufO(j), ld_o, sdo.n, ld_q0, N, tid);
-    if (w == 0) load_ld_async(bufLD(j), LSEg + ld_row, Dg + ld_row, ld_q0, N, lane);
+    load_tile_async<D, kBQ, 256, true>(bufQ(j), ld_q, sq.n, ld_q0, Nq, tid);
+    load_tile_async<D, kBQ, 256, true>(bufO(j), ld_o, sdo.n, ld_q0, Nq, tid);
+    if (w == 0) load_ld_async(bufLD(j), LSEg + ld_row, Dg + ld_row, ld_q0, Nq, lane);
     if (ld_q0 == q_lo) {
       ld_q += sq.h;
       ld_o += sdo.h;
-      ld_row += N;
+      ld_row += Nq;
     }
     ld_q0 = next_q0(ld_q0);
   };
   // A step needs the mask when some (key, query) pair of this wave is not
-  // visible: causal diagonal, ragged query block, ragged key block.
+  // visible: a band edge, a ragged query block, a ragged key block.
   auto needs_mask = [&](int q0) {
-    return (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N) || (q0 + kBQ > N);
+    if constexpr (BAND)
+      return !(kw0 - band.off >= q0 + kBQ - 1 - band.wl && kw0 + 31 - band.off <= q0 + band.wr &&
+               kw0 + 32 <= Nk && q0 + kBQ <= Nq);
+    else
+      return (kw0 + 32 > Nk) || (q0 + kBQ > Nq);
   };
+  // the queries that see this lane's key: qmin_l .. qmax_l
+  int qmin_l, qmax_l;
+  if constexpr (BAND) {
+    qmin_l = key_l - band.off - band.wr;
+    qmax_l = key_l < Nk ? min(Nq - 1, key_l - band.off + band.wl) : -1;
+  } else {
+    qmin_l = 0;
+    qmax_l = key_l < Nk ? Nq - 1 : -1;
+  }
 
   issue_loads(0);
   if (nsteps > 1) issue_loads(1);
@@ -157,7 +208,7 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 a = {0, 0, 0, 0}, c = {0, 0, 0, 0};
-    if (key_l < N) {
+    if (key_l < Nk) {
       a = *(const u32x4*)(Kh + (size_t)key_l * sk.n + ks * 16 + hi * 8);
       c = *(const u32x4*)(Vh + (size_t)key_l * sv.n + ks * 16 + hi * 8);
     }
@@ -193,10 +244,11 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
       }
     }
   };
-  // ---- P = exp2(S c - L log2 e), dS = P (dP - D), packed bf16 (masked
-  // entries: exponent -inf, P = 0); 4 queries (one g4 group) at a time
-  auto p_ds_part = [&](const f32x16& s, const f32x16& dp, const float* sLD, int q0, int g4, u32x4* oP, u32x4* oS,
-                       auto masked_tag) __attribute__((always_inline)) {
+  // ---- P = exp2(S c - L log2 e) (ALiBi: minus slope |i + off - j| log2 e),
+  // dS = P (dP - D), packed bf16 (masked entries: exponent -inf, P = 0); 4
+  // queries (one g4 group) at a time
+  auto p_ds_part = [&](const f32x16& s, const f32x16& dp, const float* sLD, int q0, float nslope, int g4,
+                       u32x4* oP, u32x4* oS, auto masked_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int qi = 8 * g4 + 4 * hi;
     const f32x4 L4 = *(const f32x4*)(sLD + qi);
@@ -206,9 +258,13 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * g4 + e;
       float arg = __builtin_fmaf(s[i], scale_log2, -L4[e] * kLog2e);
+      if constexpr (ALIBI) {
+        const float dist = (float)(q0 + qi + band.off - key_l) + (float)e;  // i + off - j
+        arg = __builtin_fmaf(nslope, __builtin_fabsf(dist), arg);
+      }
       if constexpr (MASKED) {
         const int q = q0 + qi + e;
-        arg = ((CAUSAL && key_l > q) || key_l >= N || q >= N) ? -INFINITY : arg;
+        arg = (q < qmin_l || q > qmax_l) ? -INFINITY : arg;
       }
       p[e] = fast_exp2(arg);
       ds[e] = p[e] * (dp[i] - D4[e]);
@@ -241,17 +297,21 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
     for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
   };
 
+  // ALiBi slope (negated, times log2 e) of the query head of a step
+  auto slope_of = [&](int h) { return ALIBI ? -slopes[h] * kLog2e : 0.f; };
+
   // prologue: P, dS of step 0
   wait_loads_and_sync();
   {
     f32x16 s, dp;
     s_dp(sQ0, sO0, s, dp);
+    const float ns = slope_of(h0);
     if (needs_mask(q_hi)) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) p_ds_part(s, dp, sLD0, q_hi, g4, pP, pS, std::true_type{});
+      for (int g4 = 0; g4 < 4; ++g4) p_ds_part(s, dp, sLD0, q_hi, ns, g4, pP, pS, std::true_type{});
     } else {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) p_ds_part(s, dp, sLD0, q_hi, g4, pP, pS, std::false_type{});
+      for (int g4 = 0; g4 < 4; ++g4) p_ds_part(s, dp, sLD0, q_hi, ns, g4, pP, pS, std::false_type{});
     }
   }
 
@@ -259,7 +319,7 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
   // the P / dS work of step j+1 interleaved between them (matrix core and
   // vector ALU busy at once); the loads of step j+2 go to the third buffer
   // meanwhile.
-  auto iteration = [&](int j, int nq0, auto masked_tag) __attribute__((always_inline)) {
+  auto iteration = [&](int j, int nq0, float ns, auto masked_tag) __attribute__((always_inline)) {
     f32x16 s, dp;
     s_dp(bufQ(j + 1), bufO(j + 1), s, dp);
     u32x4 nP[2], nS[2];
@@ -272,7 +332,7 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
       for (int db = 0; db < DB; ++db) {
         dvdk_part(cQ, cO, s2, db);
         const int part = s2 * DB + db;  // spread the four P / dS groups evenly
-        if (part % (2 * DB / 4) == 0) p_ds_part(s, dp, nLD, nq0, part / (2 * DB / 4), nP, nS, masked_tag);
+        if (part % (2 * DB / 4) == 0) p_ds_part(s, dp, nLD, nq0, ns, part / (2 * DB / 4), nP, nS, masked_tag);
       }
     }
     pP[0] = nP[0];
@@ -296,16 +356,19 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
       __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU
     }
   };
-  int nq0 = q_hi;  // query block of step j + 1 (after the update below)
+  int nq0 = q_hi;  // query block and head of step j + 1 (after the update below)
+  int nh = h0;
   for (int j = 0; j + 1 < nsteps; ++j) {
     pin_acc();
     wait_loads_and_sync();  // step j+1 landed; every wave is done with step j-1's buffer
     if (j + 2 < nsteps) issue_loads(j + 2);
+    if (ALIBI && nq0 == q_lo) ++nh;
     nq0 = next_q0(nq0);
+    const float ns = slope_of(nh);
     if (needs_mask(nq0))
-      iteration(j, nq0, std::true_type{});
+      iteration(j, nq0, ns, std::true_type{});
     else
-      iteration(j, nq0, std::false_type{});
+      iteration(j, nq0, ns, std::false_type{});
     pin_acc();
   }
   // last step: dV / dK only
@@ -324,7 +387,7 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kw0 + 8 * (i / 4) + 4 * hi + (i % 4);
-        if (key < N) {
+        if (key < Nk) {
           dKg[b * sdk.b + hk * sdk.h + (size_t)key * sdk.n + d] =
               (uint16_t)(pack_bf16x2(dk[db][i] * scale, 0.f) & 0xffffu);
           dVg[b * sdv.b + hk * sdv.h + (size_t)key * sdv.n + d] = (uint16_t)(pack_bf16x2(dv[db][i], 0.f) & 0xffffu);
@@ -332,15 +395,15 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
       }
     }
   } else {
-    float* pk = part + (size_t)unit * N * D;
-    float* pv = pk + (size_t)BHkv * split * N * D;
+    float* pk = part + (size_t)unit * Nk * D;
+    float* pv = pk + (size_t)BHkv * split * Nk * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int d = db * 32 + l32;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kw0 + 8 * (i / 4) + 4 * hi + (i % 4);
-        if (key < N) {
+        if (key < Nk) {
           pk[(size_t)key * D + d] = dk[db][i];
           pv[(size_t)key * D + d] = dv[db][i];
         }
@@ -389,32 +452,39 @@ kv_reduce_kernel(const float* __restrict__ part, uint16_t* __restrict__ dKg, uin
 
 
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 static int launch(const BwdArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
-  const long long rows = (long long)a.B * a.H * a.N;
+  const long long rows = (long long)a.B * a.H * a.Nq;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL((pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a.o, a.dO,
-                     a.delta, rows, a.H, a.N, a.so, a.sdo);
-  const int nkb = bwd_key_blocks(a.N);
+                     a.delta, rows, a.H, a.Nq, a.so, a.sdo);
+  const int nkb = bwd_key_blocks(a.Nk);
   static_assert(kBKC == 128, "bwd_key_blocks assumes 128-key blocks");
   const int BHkv = a.B * a.Hkv;
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3((unsigned)(nkb * BHkv * a.split)), dim3(256), 0, st, a.q, a.k,
-                     a.v, a.dO, a.lse, a.delta, a.dk, a.dv, a.part, BHkv, a.H, a.H / a.Hkv, a.split, a.N, nkb,
-                     a.scale, a.scale * kLog2e, a.sq, a.sk, a.sv, a.sdo, a.sdk, a.sdv);
+  hipLaunchKernelGGL((dkdv_kernel<D, MASK>), dim3((unsigned)(nkb * BHkv * a.split)), dim3(256), 0, st, a.q, a.k,
+                     a.v, a.dO, a.lse, a.delta, a.dk, a.dv, a.part, BHkv, a.H, a.H / a.Hkv, a.split, a.Nq, a.Nk,
+                     nkb, a.scale, a.scale * kLog2e, a.band, a.slopes, a.sq, a.sk, a.sv, a.sdo, a.sdk, a.sdv);
   if (hipGetLastError() != hipSuccess) return 1;
   if (a.split > 1) {
-    const long long kv_rows = (long long)BHkv * a.N;
+    const long long kv_rows = (long long)BHkv * a.Nk;
     hipLaunchKernelGGL((kv_reduce_kernel<D>), dim3((unsigned)((kv_rows + RPB - 1) / RPB)), dim3(256), 0, st,
-                       a.part, a.dk, a.dv, kv_rows, a.Hkv, a.split, a.N, a.scale, a.sdk, a.sdv);
+                       a.part, a.dk, a.dv, kv_rows, a.Hkv, a.split, a.Nk, a.scale, a.sdk, a.sdv);
     if (hipGetLastError() != hipSuccess) return 1;
   }
   return launch_bwd_dq(a);
 }
 
-int launch_bwd(const BwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch<128, true>(a) : launch<128, false>(a);
-  return a.causal ? launch<64, true>(a) : launch<64, false>(a);
+template <int D>
+static int launch_d(const BwdArgs& a) {
+  switch (mask_mode(a.band, a.slopes)) {
+    case kMaskNone: return launch<D, kMaskNone>(a);
+    case kMaskCausal:  // the band instance (see dkdv_kernel)
+    case kMaskBand: return launch<D, kMaskBand>(a);
+    default: return launch<D, kMaskBandAlibi>(a);
+  }
 }
+
+int launch_bwd(const BwdArgs& a) { return a.d == 128 ? launch_d<128>(a) : launch_d<64>(a); }
 
 }  // namespace fa

@@ -27,15 +27,20 @@ constexpr int kQThreads = kQNW * 64;
 
 using namespace bwd;
 
-template <int D, bool CAUSAL>
+// Masks as in the forward (the band of keys i + off - wl .. i + off + wr of
+// 0 .. Nk - 1; kMaskBandAlibi adds -slope_h |i + off - j| to the scaled
+// scores; kMaskNone and kMaskCausal keep the fixed arithmetic).
+template <int D, int MASK>
 __global__ void __launch_bounds__(kQThreads, 1)
 dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
           const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
-          uint16_t* __restrict__ dQg, int BH, int H, int group, int N, int nqb, float scale, float scale_log2,
-          Strides sq, Strides sk, Strides sv, Strides sdo, Strides sdq) {
+          uint16_t* __restrict__ dQg, int BH, int H, int group, int Nq, int Nk, int nqb, float scale,
+          float scale_log2, Band band, const float* __restrict__ slopes, Strides sq, Strides sk, Strides sv,
+          Strides sdo, Strides sdq) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = kQBC * D;
+  constexpr bool BAND = MASK >= kMaskBand, CAUSAL = MASK == kMaskCausal, ALIBI = MASK == kMaskBandAlibi;
 
   __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
@@ -43,40 +48,66 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
   __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  // The wave index is uniform. Under a general band, readfirstlane lets the
+  // per-wave bounds live in scalar registers (else they spill); the fixed
+  // masks schedule better without it.
+  const int lane = tid & 63, w = BAND ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6, l32 = lane & 31,
+            hi = lane >> 5;
   const int g = lane >> 4, i16 = lane & 15;
 
   const int wid = xcd_work_id(nqb * BH);
   const int bh = wid / nqb;
-  const int qblk = CAUSAL ? nqb - 1 - (wid % nqb) : (wid % nqb);
+  const int qblk = MASK != kMaskNone ? nqb - 1 - (wid % nqb) : (wid % nqb);
   const int b = bh / H, h = bh % H, hk = h / group;  // query head h reads K/V head h / group
   const uint16_t* Kh = Kg + b * sk.b + hk * sk.h;
   const uint16_t* Vh = Vg + b * sv.b + hk * sv.h;
-  const int qw0 = qblk * kQBR + w * 32;
+  const int q0 = qblk * kQBR;
+  const int qw0 = q0 + w * 32;
   const int qrow = qw0 + l32;
 
-  const int kend = CAUSAL ? min(N, qblk * kQBR + kQBR) : N;
-  const int ntiles = (kend + kQBC - 1) / kQBC;
-  const int wlast = CAUSAL ? min(ntiles - 1, (qw0 + 31) / kQBC) : ntiles - 1;
+  // key tiles t0 .. t1 - 1 cover the band of the block's rows, wfirst .. wlast
+  // that of this wave's rows (none when they are all past Nq)
+  int t0 = 0, t1, wfirst = 0, wlast;
+  if constexpr (BAND) {
+    const int qlast = min(q0 + kQBR, Nq) - 1;
+    const int blo = max(0, q0 + band.off - band.wl);
+    const int bhi = min(Nk - 1, qlast + band.off + band.wr);
+    t0 = blo / kQBC;
+    t1 = bhi >= blo ? bhi / kQBC + 1 : t0;
+    const int wqlast = min(qw0 + 32, Nq) - 1;
+    const int wlo = max(0, qw0 + band.off - band.wl);
+    const int whi = min(Nk - 1, wqlast + band.off + band.wr);
+    wfirst = wlo / kQBC;
+    wlast = (wqlast >= qw0 && whi >= wlo) ? whi / kQBC : -1;
+  } else {
+    const int kend = CAUSAL ? min(Nk, q0 + kQBR) : Nk;
+    t1 = (kend + kQBC - 1) / kQBC;
+    wlast = CAUSAL ? min(t1 - 1, (qw0 + 31) / kQBC) : t1 - 1;
+  }
+  float nslope = 0.f;
+  if constexpr (ALIBI) nslope = -slopes[h] * kLog2e;
 
-  load_tile_async<D, kQBC, kQThreads, true>(sK0, Kh, sk.n, 0, N, tid);
-  load_tile_async<D, kQBC, kQThreads, true>(sV0, Vh, sv.n, 0, N, tid);
+  if (t1 > t0) {
+    load_tile_async<D, kQBC, kQThreads, true>(sK0, Kh, sk.n, t0 * kQBC, Nk, tid);
+    load_tile_async<D, kQBC, kQThreads, true>(sV0, Vh, sv.n, t0 * kQBC, Nk, tid);
+  }
 
   // Q and dO as B operands of S^T = K Q^T and dP^T = V dO^T
   bf16x8 qf[KS], of[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 a = {0, 0, 0, 0}, e = {0, 0, 0, 0};
-    if (qrow < N) {
+    if (qrow < Nq) {
       a = *(const u32x4*)(Qg + b * sq.b + h * sq.h + (size_t)qrow * sq.n + ks * 16 + hi * 8);
       e = *(const u32x4*)(dOg + b * sdo.b + h * sdo.h + (size_t)qrow * sdo.n + ks * 16 + hi * 8);
     }
     qf[ks] = as_bf16x8(a);
     of[ks] = as_bf16x8(e);
   }
-  // rows past N: L = +inf gives P = 0
-  const float Lq = qrow < N ? LSEg[(size_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float Dq = qrow < N ? Dg[(size_t)bh * N + qrow] : 0.f;
+  // rows past Nq: L = +inf gives P = 0 (rows that see no key have L = -inf and
+  // lie only in masked tiles, where P is set to 0)
+  const float Lq = qrow < Nq ? LSEg[(size_t)bh * Nq + qrow] * kLog2e : INFINITY;
+  const float Dq = qrow < Nq ? Dg[(size_t)bh * Nq + qrow] : 0.f;
 
   f32x16 acc[DB];
 #pragma unroll
@@ -112,10 +143,21 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * h2 + j;
-          float pv = fast_exp2(__builtin_fmaf(s[i], scale_log2, -Lq));
+          float arg = __builtin_fmaf(s[i], scale_log2, -Lq);
+          if constexpr (ALIBI) {
+            const float dist = (float)(k0 + kb * 32 + 4 * hi - qrow - band.off) + (float)(8 * (i / 4) + (i % 4));
+            arg = __builtin_fmaf(nslope, __builtin_fabsf(dist), arg);
+          }
+          float pv = fast_exp2(arg);
           if constexpr (MASKED) {
             const int key = k0 + kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
-            if ((CAUSAL && key > qrow) || key >= N) pv = 0.f;
+            if constexpr (BAND) {
+              // this lane's visible keys are qr + off - wl .. qr + off + wr
+              const int qr = qw0 + l32;
+              if (key < qr + band.off - band.wl || key > qr + band.off + band.wr || key >= Nk) pv = 0.f;
+            } else {
+              if ((CAUSAL && key > qrow) || key >= Nk) pv = 0.f;
+            }
           }
           ds[j] = pv * (dp[i] - Dq);
         }
@@ -137,25 +179,31 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
   };
 
   // Buffers alternate by tile parity (not unrolled, for the same reason).
-  for (int t = 0; t < ntiles; ++t) {
-    const bool odd = t & 1;
+  for (int t = t0; t < t1; ++t) {
+    const bool odd = (t - t0) & 1;
     wait_loads_and_sync();  // tile t landed; every wave finished tile t-1
-    if (t + 1 < ntiles) {
-      load_tile_async<D, kQBC, kQThreads, true>(odd ? sK0 : sK1, Kh, sk.n, (t + 1) * kQBC, N, tid);
-      load_tile_async<D, kQBC, kQThreads, true>(odd ? sV0 : sV1, Vh, sv.n, (t + 1) * kQBC, N, tid);
+    if (t + 1 < t1) {
+      load_tile_async<D, kQBC, kQThreads, true>(odd ? sK0 : sK1, Kh, sk.n, (t + 1) * kQBC, Nk, tid);
+      load_tile_async<D, kQBC, kQThreads, true>(odd ? sV0 : sV1, Vh, sv.n, (t + 1) * kQBC, Nk, tid);
     }
-    if (t > wlast) continue;  // this wave's rows see none of these keys
+    if ((BAND && t < wfirst) || t > wlast) continue;  // this wave's rows see none of these keys
     const int k0 = t * kQBC;
     const uint16_t* sK = odd ? sK1 : sK0;
     const uint16_t* sV = odd ? sV1 : sV0;
-    if ((CAUSAL && k0 + kQBC - 1 > qw0) || k0 + kQBC > N)
+    // mask unless every row of this wave sees the whole tile
+    bool masked;
+    if constexpr (BAND)
+      masked = !(k0 >= qw0 + 31 + band.off - band.wl && k0 + kQBC - 1 <= qw0 + band.off + band.wr && k0 + kQBC <= Nk);
+    else
+      masked = (CAUSAL && k0 + kQBC - 1 > qw0) || k0 + kQBC > Nk;
+    if (masked)
       tile(t, sK, sV, std::true_type{});
     else
       tile(t, sK, sV, std::false_type{});
   }
 
   // ---- dQ = scale dQ^T^T, bf16 (lane = query, d over the accumulator rows)
-  if (qrow < N) {
+  if (qrow < Nq) {
     uint16_t* row = dQg + b * sdq.b + h * sdq.h + (size_t)qrow * sdq.n;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -169,19 +217,26 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 static int launch_dq(const BwdArgs& a) {
   const int BH = a.B * a.H;
-  const int nqb = (a.N + kQBR - 1) / kQBR;
-  hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3((unsigned)(nqb * BH)), dim3(kQThreads), 0, (hipStream_t)a.stream,
-                     a.q, a.k, a.v, a.dO, a.lse, a.delta, a.dq, BH, a.H, a.H / a.Hkv, a.N, nqb, a.scale,
-                     a.scale * kLog2e, a.sq, a.sk, a.sv, a.sdo, a.sdq);
+  const int nqb = (a.Nq + kQBR - 1) / kQBR;
+  hipLaunchKernelGGL((dq_kernel<D, MASK>), dim3((unsigned)(nqb * BH)), dim3(kQThreads), 0, (hipStream_t)a.stream,
+                     a.q, a.k, a.v, a.dO, a.lse, a.delta, a.dq, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale,
+                     a.scale * kLog2e, a.band, a.slopes, a.sq, a.sk, a.sv, a.sdo, a.sdq);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-int launch_bwd_dq(const BwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_dq<128, true>(a) : launch_dq<128, false>(a);
-  return a.causal ? launch_dq<64, true>(a) : launch_dq<64, false>(a);
+template <int D>
+static int launch_dq_d(const BwdArgs& a) {
+  switch (mask_mode(a.band, a.slopes)) {
+    case kMaskNone: return launch_dq<D, kMaskNone>(a);
+    case kMaskCausal: return launch_dq<D, kMaskCausal>(a);
+    case kMaskBand: return launch_dq<D, kMaskBand>(a);
+    default: return launch_dq<D, kMaskBandAlibi>(a);
+  }
 }
+
+int launch_bwd_dq(const BwdArgs& a) { return a.d == 128 ? launch_dq_d<128>(a) : launch_dq_d<64>(a); }
 
 }  // namespace fa

@@ -65,15 +65,23 @@ __device__ __forceinline__ void wait_loads_and_sync() {
 
 }  // namespace
 
-template <int D, bool CAUSAL>
+// Masks: query i sees keys i + off - wl .. i + off + wr of 0 .. Nk - 1 (the
+// band; causal, sliding windows and cross-attention are all bands). Tiles
+// outside a Q-block's band are never loaded, tiles outside a wave's band are
+// skipped, and only tiles that cut the band's edges (or the end of the keys)
+// are masked element by element. With ALiBi (kMaskBandAlibi) the scaled
+// score of query i and key j gets -slope_h |i + off - j|. kMaskNone and
+// kMaskCausal are the no-mask and plain causal bands with fixed arithmetic.
+template <int D, int MASK>
 __global__ void __launch_bounds__(kThreads, 1)
 fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
            const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og, float* __restrict__ LSEg,
-           int BH, int H, int group, int N, int nqb, float scale_log2, Strides sq, Strides sk, Strides sv,
-           Strides so) {
+           int BH, int H, int group, int Nq, int Nk, int nqb, float scale_log2, Band band,
+           const float* __restrict__ slopes, Strides sq, Strides sk, Strides sv, Strides so) {
   constexpr int KS = D / 16;        // k-steps of the S product
   constexpr int DB = D / 32;        // 32-row d blocks of O^T
   constexpr int TILE = kBC * D;     // elements of one K or V tile
+  constexpr bool BAND = MASK >= kMaskBand, CAUSAL = MASK == kMaskCausal, ALIBI = MASK == kMaskBandAlibi;
 
   // Four separate arrays so that the compiler can tell the buffer being filled
   // by the direct loads from the one being read.
@@ -83,54 +91,81 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  // the wave index is uniform: readfirstlane lets every per-wave bound live in
+  // scalar registers and keeps the per-tile branches uniform
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6), l32 = lane & 31, hi = lane >> 5;
   const int g = lane >> 4, i16 = lane & 15;
 
   // Work id: one head's Q-blocks run together on one XCD (blocks are dispatched
   // round-robin over the 8 XCDs) so its K/V stay in that XCD's L2; inside a
-  // head, the heaviest causal Q-blocks go first.
+  // head, the last Q-blocks (the heaviest under a causal band) go first.
   const int total = nqb * BH;
   int wid = (int)blockIdx.x;
   if ((total & 7) == 0) wid = (wid & 7) * (total >> 3) + (wid >> 3);
   const int bh = wid / nqb;
-  const int qblk = CAUSAL ? nqb - 1 - (wid % nqb) : (wid % nqb);
+  const int qblk = MASK != kMaskNone ? nqb - 1 - (wid % nqb) : (wid % nqb);
   const int b = bh / H, h = bh % H, hk = h / group;  // query head h reads K/V head h / group
   const uint16_t* Qh = Qg + b * sq.b + h * sq.h;
   const uint16_t* Kh = Kg + b * sk.b + hk * sk.h;
   const uint16_t* Vh = Vg + b * sv.b + hk * sv.h;
-  const int qw0 = qblk * kBR + w * kQW;  // first query row of this wave
-  const int qrow = qw0 + l32;            // this lane's query
+  const int q0 = qblk * kBR;
+  const int qw0 = q0 + w * kQW;  // first query row of this wave
+  const int qrow = qw0 + l32;    // this lane's query
 
-  const int kend = CAUSAL ? min(N, qblk * kBR + kBR) : N;
-  const int ntiles = (kend + kBC - 1) / kBC;
-  // last tile this wave needs (causal: the one holding its diagonal)
-  const int wlast = CAUSAL ? min(ntiles - 1, (qw0 + kQW - 1) / kBC) : ntiles - 1;
+  // Key tiles t0 .. t1 - 1 hold the band of the block's rows; this wave's rows
+  // need tiles wfirst .. wlast of them (none when its rows are all past Nq).
+  int t0 = 0, t1, wfirst = 0, wlast, klo = 0, khi = 0;
+  if constexpr (BAND) {
+    const int qlast = min(q0 + kBR, Nq) - 1;
+    const int blo = max(0, q0 + band.off - band.wl);
+    const int bhi = min(Nk - 1, qlast + band.off + band.wr);
+    t0 = blo / kBC;
+    t1 = bhi >= blo ? bhi / kBC + 1 : t0;
+    const int wqlast = min(qw0 + kQW, Nq) - 1;
+    const int wlo = max(0, qw0 + band.off - band.wl);
+    const int whi = min(Nk - 1, wqlast + band.off + band.wr);
+    wfirst = wlo / kBC;
+    wlast = (wqlast >= qw0 && whi >= wlo) ? whi / kBC : -1;
+    klo = qrow + band.off - band.wl;  // this lane's visible keys
+    khi = min(Nk - 1, qrow + band.off + band.wr);
+  } else {
+    const int kend = CAUSAL ? min(Nk, q0 + kBR) : Nk;
+    t1 = (kend + kBC - 1) / kBC;
+    wlast = CAUSAL ? min(t1 - 1, (qw0 + kQW - 1) / kBC) : t1 - 1;  // causal: the diagonal tile
+  }
+  float nslope = 0.f;  // ALiBi slope times log2 e, negated
+  if constexpr (ALIBI) nslope = -slopes[h] * kLog2e;
 
-  load_tile_async<D, false>(sK0, Kh, sk.n, 0, N, tid);
-  load_tile_async<D, true>(sV0, Vh, sv.n, 0, N, tid);
+  if (t1 > t0) {
+    load_tile_async<D, false>(sK0, Kh, sk.n, t0 * kBC, Nk, tid);
+    load_tile_async<D, true>(sV0, Vh, sv.n, t0 * kBC, Nk, tid);
+  }
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[q][16 ks + 8 hi .. +7].
   bf16x8 qf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     u32x4 u = {0, 0, 0, 0};
-    if (qrow < N) u = *(const u32x4*)(Qh + (size_t)qrow * sq.n + ks * 16 + hi * 8);
+    if (qrow < Nq) u = *(const u32x4*)(Qh + (size_t)qrow * sq.n + ks * 16 + hi * 8);
     qf[ks] = as_bf16x8(u);
   }
 
   f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  // Under a general band m starts finite so that a row whose first tiles are
+  // all masked keeps p = exp2(-inf - m) = 0 (no inf - inf) until it sees a
+  // key; otherwise every row sees a key in its first tile.
+  float m = BAND ? -1e30f : -INFINITY, l = 0.f;
 
   // One tile: K(t), V(t) are in (sK, sV); the loads of tile t+1 go to (nK, nV).
   auto tile = [&](int t, const uint16_t* sK, const uint16_t* sV, uint16_t* nK, uint16_t* nV) {
     wait_loads_and_sync();  // tile t landed; every wave finished tile t-1
-    if (t + 1 < ntiles) {
-      load_tile_async<D, false>(nK, Kh, sk.n, (t + 1) * kBC, N, tid);
-      load_tile_async<D, true>(nV, Vh, sv.n, (t + 1) * kBC, N, tid);
+    if (t + 1 < t1) {
+      load_tile_async<D, false>(nK, Kh, sk.n, (t + 1) * kBC, Nk, tid);
+      load_tile_async<D, true>(nV, Vh, sv.n, (t + 1) * kBC, Nk, tid);
     }
-    if (t > wlast) return;  // this wave's rows see none of these keys
+    if ((BAND && t < wfirst) || t > wlast) return;  // this wave's rows see none of these keys
     const int k0 = t * kBC;
 
     // ---- S^T = K Q^T: two 32-key blocks (K operands read one k-step ahead)
@@ -160,14 +195,31 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
         a[1] = an[1];
       }
     }
-    // ---- online softmax (lane-local plus one half-wave exchange)
-    if ((CAUSAL && k0 + kBC - 1 > qw0) || (k0 + kBC > N)) {
+    // ---- ALiBi: scores to the exp2 domain with the bias, -slope |i + off - j|
+    if constexpr (ALIBI) {
+      const float fb = (float)(k0 + 4 * hi - qrow - band.off);  // j - (i + off) of element 0
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s[kb][i] = __builtin_fmaf(s[kb][i], scale_log2,
+                                    nslope * __builtin_fabsf(fb + (float)(kb * 32 + 8 * (i / 4) + (i % 4))));
+    }
+    // ---- online softmax (lane-local plus one half-wave exchange); mask only
+    // tiles that some row of this wave does not see whole
+    bool masked;
+    if constexpr (BAND)
+      masked = !(k0 >= qw0 + kQW - 1 + band.off - band.wl && k0 + kBC - 1 <= qw0 + band.off + band.wr &&
+                 k0 + kBC <= Nk);
+    else
+      masked = (CAUSAL && k0 + kBC - 1 > qw0) || (k0 + kBC > Nk);
+    if (masked) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + 8 * (i / 4) + 4 * hi + (i % 4);
-          if ((CAUSAL && key > qrow) || key >= N) s[kb][i] = -INFINITY;
+          if (BAND ? (key < klo || key > khi) : ((CAUSAL && key > qrow) || key >= Nk)) s[kb][i] = -INFINITY;
         }
     }
     float mx = fmaxf(s[0][0], s[0][1]);
@@ -175,11 +227,12 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = (kb == 0 ? 2 : 0); i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
-    mx = fmaxf(mx, other_half(mx)) * scale_log2;
-    // finite: key 0 is visible to every row and sits in tile 0. The running
-    // max is replaced (and O, l rescaled) only when some row's max exceeds it
-    // by more than kRescaleSlack: until then p <= 2^kRescaleSlack, and O and l
-    // share the same stale max, so O / l and the LSE are unchanged.
+    mx = fmaxf(mx, other_half(mx));
+    if constexpr (!ALIBI) mx *= scale_log2;
+    // The running max is replaced (and O, l rescaled) only when some row's max
+    // exceeds it by more than kRescaleSlack: until then p <= 2^kRescaleSlack,
+    // and O and l share the same stale max, so O / l and the LSE are unchanged.
+    // A row that has seen no key yet has mx = -inf and keeps m.
     if (__any(mx > m + kRescaleSlack)) {
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
@@ -197,7 +250,10 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          p[j] = fast_exp2(__builtin_fmaf(s[kb][8 * h2 + j], scale_log2, -m));
+          if constexpr (ALIBI)
+            p[j] = fast_exp2(s[kb][8 * h2 + j] - m);
+          else
+            p[j] = fast_exp2(__builtin_fmaf(s[kb][8 * h2 + j], scale_log2, -m));
           rs += p[j];
         }
         pb[kb][h2] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
@@ -227,17 +283,18 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     }
   };
 
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
+  int t = t0;
+  for (; t + 1 < t1; t += 2) {
     tile(t, sK0, sV0, sK1, sV1);
     tile(t + 1, sK1, sV1, sK0, sV0);
   }
-  if (t < ntiles) tile(t, sK0, sV0, sK1, sV1);
+  if (t < t1) tile(t, sK0, sV0, sK1, sV1);
 
-  // ---- epilogue: divide once by l, store O (bf16) and LSE (natural log)
+  // ---- epilogue: divide once by l, store O (bf16) and LSE (natural log); a
+  // row that saw no key stores O = 0 and LSE = -inf
   const float lt = l + other_half(l);
-  const float inv = 1.0f / lt;
-  if (qrow < N) {
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (qrow < Nq) {
     uint16_t* orow = Og + b * so.b + h * so.h + (size_t)qrow * so.n;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -248,24 +305,31 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
                           pack_bf16x2(acc[db][4 * g4 + 2] * inv, acc[db][4 * g4 + 3] * inv)};
         *(u32x2*)(orow + d) = pk;
       }
-    if (hi == 0) LSEg[(size_t)bh * N + qrow] = (m + __log2f(lt)) * kLn2;
+    if (hi == 0) LSEg[(size_t)bh * Nq + qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 static int launch(const FwdArgs& a) {
-  const int nqb = (a.N + kBR - 1) / kBR;
+  const int nqb = (a.Nq + kBR - 1) / kBR;
   const int BH = a.B * a.H;
   const dim3 grid((unsigned)(nqb * BH)), block(kThreads);
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL>), grid, block, 0, (hipStream_t)a.stream,
-                     a.q, a.k, a.v, a.o, a.lse, BH, a.H, a.H / a.Hkv, a.N, nqb, a.scale * kLog2e, a.sq, a.sk, a.sv,
-                     a.so);
+  hipLaunchKernelGGL((fwd_kernel<D, MASK>), grid, block, 0, (hipStream_t)a.stream,
+                     a.q, a.k, a.v, a.o, a.lse, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.band,
+                     a.slopes, a.sq, a.sk, a.sv, a.so);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-int launch_fwd(const FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch<128, true>(a) : launch<128, false>(a);
-  return a.causal ? launch<64, true>(a) : launch<64, false>(a);
+template <int D>
+static int launch_d(const FwdArgs& a) {
+  switch (mask_mode(a.band, a.slopes)) {
+    case kMaskNone: return launch<D, kMaskNone>(a);
+    case kMaskCausal: return launch<D, kMaskCausal>(a);
+    case kMaskBand: return launch<D, kMaskBand>(a);
+    default: return launch<D, kMaskBandAlibi>(a);
+  }
 }
+
+int launch_fwd(const FwdArgs& a) { return a.d == 128 ? launch_d<128>(a) : launch_d<64>(a); }
 
 }  // namespace fa

@@ -15,6 +15,26 @@ inline Strides contiguous_strides(int H, int N, int d) {
   return Strides{(long long)H * N * d, (long long)N * d, (long long)d};
 }
 
+// Keys visible to query i (of Nq, against Nk keys): i + off - wl ..
+// i + off + wr, intersected with 0 .. Nk - 1. off = Nk - Nq aligns the last
+// query with the last key; causal is wr = 0; kOpen leaves a side unbounded.
+constexpr int kOpen = 1 << 30;
+struct Band {
+  int off, wl, wr;
+};
+
+// Kernel instances by mask: no mask, causal with Nq = Nk (the band (open, 0),
+// off = 0), any band, any band with ALiBi. The first two keep the simplest
+// index arithmetic (their kernels run at the register limit, where every
+// extra live value costs).
+enum MaskMode { kMaskNone = 0, kMaskCausal = 1, kMaskBand = 2, kMaskBandAlibi = 3 };
+inline MaskMode mask_mode(const Band& b, const float* slopes) {
+  if (slopes) return kMaskBandAlibi;
+  if (b.wl == kOpen && b.wr == kOpen) return kMaskNone;
+  if (b.wl == kOpen && b.wr == 0 && b.off == 0) return kMaskCausal;
+  return kMaskBand;
+}
+
 // H query heads share Hkv key/value heads: query head h reads K/V head
 // h / (H / Hkv) (Hkv divides H; Hkv = H is plain multi-head attention).
 struct FwdArgs {
@@ -22,8 +42,10 @@ struct FwdArgs {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* o;
-  float* lse;  // contiguous [B, H, N]
-  int B, H, Hkv, N, d, causal;
+  float* lse;  // contiguous [B, H, Nq]
+  int B, H, Hkv, Nq, Nk, d;
+  Band band;
+  const float* slopes;  // ALiBi slopes [H] (device), or null
   float scale;
   Strides sq, sk, sv, so;
   void* stream;
@@ -35,12 +57,14 @@ struct BwdArgs {
   const uint16_t* v;
   const uint16_t* o;
   const uint16_t* dO;
-  const float* lse;  // contiguous [B, H, N]
+  const float* lse;  // contiguous [B, H, Nq]
   uint16_t* dq;
   uint16_t* dk;      // [B, Hkv, N, d] view: the sum over the query heads of each group
   uint16_t* dv;
-  float* delta;      // workspace: fp32 D [B, H, N]
-  int B, H, Hkv, N, d, causal;
+  float* delta;      // workspace: fp32 D [B, H, Nq]
+  int B, H, Hkv, Nq, Nk, d;
+  Band band;
+  const float* slopes;  // ALiBi slopes [H] (device), or null
   float scale;
   Strides sq, sk, sv, so, sdo, sdq, sdk, sdv;
   void* stream;
@@ -90,11 +114,11 @@ inline int bwd_key_blocks(int N) { return (N + 127) / 128; }
 // heads: each sums the gradients of group / split query heads and, for
 // split > 1, writes fp32 partials that a reduction adds up. The smallest
 // divisor of the group that gives at least 256 workgroups (one per CU), or
-// 1024 when causal (so that the uneven causal blocks balance), else the
+// 1024 when the band is bounded (so that uneven key blocks balance), else the
 // whole group.
-inline int bwd_kv_split(int B, int H_kv, int group, int N, int causal) {
+inline int bwd_kv_split(int B, int H_kv, int group, int N, bool uneven) {
   const long long units = (long long)bwd_key_blocks(N) * B * H_kv;
-  const long long want = causal ? 1024 : 256;
+  const long long want = uneven ? 1024 : 256;
   for (int s = 1; s < group; ++s)
     if (group % s == 0 && units * s >= want) return s;
   return group;

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 enum fa_status {
   FA_OK = 0,
@@ -50,7 +50,8 @@ enum fa_status {
   FA_ERR_DEVICE = 6,    /* no HIP device, or the current device is not gfx950 */
   FA_ERR_ALIAS = 7,     /* an output overlaps an input, another output or itself */
   FA_ERR_LAUNCH = 8,    /* the kernel launch failed (hipGetLastError) */
-  FA_ERR_ARG = 9        /* causal not 0/1, scale not finite and positive, a stride < 1, or a row stride >= 2^31 */
+  FA_ERR_ARG = 9        /* causal not 0/1, a window side < -1 or > 2^24, scale not finite and positive,
+                           a stride < 1, or a row stride >= 2^31 */
 };
 
 /*
@@ -152,6 +153,61 @@ int fa_bwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, cons
                    const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
                    int B, int H, int H_kv, int N, int d, const fa_strides* st, int causal, float scale,
                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Masks beyond causal, and queries and keys of different lengths ([LIB]
+ * "Cases where FlashAttention does not help": the kernels ship causal,
+ * sliding-window and ALiBi masks; cross-attention is supported). Query i of
+ * N_q is aligned with key c_i = i + N_k - N_q (the last query with the last
+ * key; c_i = i when N_q = N_k). Key j is visible to query i iff
+ *   causal = 0 or j <= c_i, and
+ *   window_left  = -1 or j >= c_i - window_left, and
+ *   window_right = -1 or j <= c_i + window_right.
+ * alibi_slopes, when not NULL, is a device fp32 [H] array (one slope per query
+ * head, finite; 4-byte aligned): the scaled score of (i, j) in head h gets
+ * -alibi_slopes[h] * |c_i - j| added before the softmax (no gradient flows to
+ * the slopes). A query with no visible key gets O = 0 and LSE = -inf, and
+ * zero gradients. A NULL mask is causal = 0, both windows -1, no ALiBi.
+ */
+typedef struct fa_mask {
+  int causal;                /* 0 or 1 */
+  int window_left;           /* -1 (unbounded) or 0 .. 2^24 */
+  int window_right;          /* -1 (unbounded) or 0 .. 2^24 */
+  const float* alibi_slopes; /* NULL or device fp32 [H] */
+} fa_mask;
+
+/*
+ * The general forward: fa_fwd_strided with N_q queries against N_k keys and
+ * a mask (above). fa_fwd_strided is the case N_q = N_k = N with
+ * {causal, -1, -1, NULL}.
+ *   q, o  : [B, H, N_q, d] views;  k, v : [B, H_kv, N_k, d] views
+ *   lse   : out, fp32 contiguous [B, H, N_q]
+ *   st    : host array of 4 views' strides (q, k, v, o), rules of fa_fwd_strided
+ *   mask  : host pointer, or NULL
+ */
+int fa_fwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+               int B, int H, int H_kv, int N_q, int N_k, int d, const fa_strides* st, const fa_mask* mask,
+               float scale, void* stream);
+
+/*
+ * Workspace bytes of fa_bwd_ext: fp32 D [B, H, N_q] rounded to 256 bytes,
+ * then for grouped heads split over workgroups the fp32 partial dK, dV
+ * (2 x B x H_kv x s x N_k x d x 4 bytes, s dividing H / H_kv; see
+ * fa_bwd_strided_workspace_bytes). 0 for invalid arguments.
+ */
+size_t fa_bwd_ext_workspace_bytes(int B, int H, int H_kv, int N_q, int N_k, int d, const fa_mask* mask);
+
+/*
+ * The general backward, matching fa_fwd_ext (o and lse as it produced them).
+ *   q, o, dO, dq : [B, H, N_q, d] views;  k, v, dk, dv : [B, H_kv, N_k, d] views
+ *   st           : host array of 8 views' strides (q, k, v, o, dO, dq, dk, dv)
+ *   ws, ws_bytes : >= fa_bwd_ext_workspace_bytes(B, H, H_kv, N_q, N_k, d, mask)
+ * Keys no query sees get dK = dV = 0. Deterministic, as fa_bwd.
+ */
+int fa_bwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+               const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+               int B, int H, int H_kv, int N_q, int N_k, int d, const fa_strides* st, const fa_mask* mask,
+               float scale, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * FP8 input path ([LIB] "FA3 — the Hopper moment", pillar 3; [LIN] "FA3

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_version_and_status_strings():
-    assert fa.abi_version() == 2
+    assert fa.abi_version() == 3
     codes = declared_status_codes()
     assert codes["FA_OK"] == 0 and len(codes) == 10
     for name, val in codes.items():
@@ -187,3 +187,61 @@ def test_strided_no_device_is_reported_after_validation():
 @pytest.mark.skipif(torch.cuda.is_available(), reason="valid-looking fake pointers must never reach a GPU")
 def test_no_device_is_reported_after_validation():
     assert _fwd() == 6
+
+
+def _mask(causal=0, left=-1, right=-1, slopes=None):
+    return ctypes.byref(fa.Mask(causal, left, right, slopes))
+
+
+def test_ext_entry_points_reject_bad_arguments():
+    """fa_fwd_ext / fa_bwd_ext: every call below fails host validation first."""
+    lib = fa.load_library()
+    B, H, Hkv, Nq, Nk, d = 1, 4, 2, 48, 80, 64
+    cq, ck = (H * Nq * d, Nq * d, d), (Hkv * Nk * d, Nk * d, d)
+    q, k, v, o, lse = (P + i * 0x100000 for i in range(5))
+    sl = P + 0x600000
+
+    def fwd(mask, **kw):
+        a = dict(q=q, k=k, v=v, o=o, lse=lse, Nq=Nq, Nk=Nk, st=_st(cq, ck, ck, cq))
+        a.update(kw)
+        return lib.fa_fwd_ext(a["q"], a["k"], a["v"], a["o"], a["lse"], B, H, Hkv, a["Nq"], a["Nk"], d, a["st"],
+                              mask, 0.125, None)
+    assert fwd(_mask(2)) == 9                               # causal not 0 / 1
+    assert fwd(_mask(0, -2)) == 9                           # window side below -1
+    assert fwd(_mask(0, 3, (1 << 24) + 1)) == 9             # window side above 2^24
+    assert fwd(_mask(0, 3, 3, sl + 2)) == 4                 # slopes not 4-byte aligned
+    assert fwd(_mask(0, 3, 3, o + 64)) == 7                 # slopes inside the output
+    assert fwd(_mask(1), Nk=0) == 2
+    assert fwd(_mask(1), st=_st(cq, ck, ck, cq[:2] + (8,))) == 7  # o rows overlap
+    ws = 0x40000000
+    need = lib.fa_bwd_ext_workspace_bytes(B, H, Hkv, Nq, Nk, d, _mask(1, 16, 0))
+    assert need >= B * H * Nq * 4
+    assert lib.fa_bwd_ext_workspace_bytes(B, H, Hkv, Nq, Nk, d, _mask(0, -5)) == 0
+    assert lib.fa_bwd_ext_workspace_bytes(B, H, 3, Nq, Nk, d, None) == 0
+    ptrs = [P + i * 0x100000 for i in range(9)]
+    st8 = _st(cq, ck, ck, cq, cq, cq, ck, ck)
+    args = ptrs + [B, H, Hkv, Nq, Nk, d, st8, _mask(1, 16, 0), 0.125, ws, need, None]
+    bad = list(args)
+    bad[19] = need - 256                                    # workspace too small
+    assert lib.fa_bwd_ext(*bad) == 5
+    bad = list(args)
+    bad[16] = _mask(1, 16, 0, ptrs[6] + 4)                  # slopes inside dq
+    assert lib.fa_bwd_ext(*bad) == 7
+    bad = list(args)
+    bad[16] = _mask(3)
+    assert lib.fa_bwd_ext(*bad) == 9
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="valid-looking fake pointers must never reach a GPU")
+def test_ext_no_device_is_reported_after_validation():
+    lib = fa.load_library()
+    B, H, Hkv, Nq, Nk, d = 2, 4, 1, 33, 300, 128
+    cq, ck = (H * Nq * d, Nq * d, d), (Hkv * Nk * d, Nk * d, d)
+    ptrs = [P + i * 0x1000000 for i in range(9)]
+    sl = P + 0x20000000
+    assert lib.fa_fwd_ext(*ptrs[:5], B, H, Hkv, Nq, Nk, d, _st(cq, ck, ck, cq), _mask(1, 100, 0, sl), 0.1,
+                          None) == 6
+    assert lib.fa_fwd_ext(*ptrs[:5], B, H, Hkv, Nq, Nk, d, _st(cq, ck, ck, cq), None, 0.1, None) == 6
+    st8 = _st(cq, ck, ck, cq, cq, cq, ck, ck)
+    need = lib.fa_bwd_ext_workspace_bytes(B, H, Hkv, Nq, Nk, d, None)
+    assert lib.fa_bwd_ext(*ptrs, B, H, Hkv, Nq, Nk, d, st8, None, 0.1, 0x40000000, need, None) == 6

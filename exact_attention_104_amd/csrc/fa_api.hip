@@ -62,6 +62,9 @@ bool scalars_ok(int causal, float scale) {
 
 bool scale_ok(float scale) { return std::isfinite(scale) && scale > 0.f; }
 
+// head dims of the bf16 kernels (the fp8 path takes 64 and 128)
+bool bf16_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
 constexpr int kMaxLen = 1 << 24;
 
 // A mask is valid with causal 0 / 1 and each window side -1 (unbounded) or
@@ -151,7 +154,7 @@ int fa_fwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t
                float scale, void* stream) {
   if (!scale_ok(scale) || !mask_ok(mask)) return FA_ERR_ARG;
   if (!q || !k || !v || !o || !lse || !st) return FA_ERR_NULL;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!bf16_head_dim(d)) return FA_ERR_HEADDIM;
   if (!shape_ok(B, H, N_q, d) || !shape_ok(B, H_kv, N_k, d) || H_kv < 1 || H % H_kv != 0) return FA_ERR_SHAPE;
   const View vq{q, B, H, N_q, d, st[0]}, vk{k, B, H_kv, N_k, d, st[1]}, vv{v, B, H_kv, N_k, d, st[2]},
       vo{o, B, H, N_q, d, st[3]};
@@ -187,12 +190,12 @@ int fa_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
-  if ((d != 64 && d != 128) || !shape_ok(B, H, N, d)) return 0;
+  if (!bf16_head_dim(d) || !shape_ok(B, H, N, d)) return 0;
   return fa::bwd_delta_bytes(B, H, N);
 }
 
 size_t fa_bwd_ext_workspace_bytes(int B, int H, int H_kv, int N_q, int N_k, int d, const fa_mask* mask) {
-  if ((d != 64 && d != 128) || !shape_ok(B, H, N_q, d) || !shape_ok(B, H_kv, N_k, d) || H_kv < 1 ||
+  if (!bf16_head_dim(d) || !shape_ok(B, H, N_q, d) || !shape_ok(B, H_kv, N_k, d) || H_kv < 1 ||
       H % H_kv != 0 || !mask_ok(mask))
     return 0;
   const int split = fa::bwd_kv_split(B, H_kv, H / H_kv, N_k, uneven(mask));
@@ -211,7 +214,7 @@ int fa_bwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v, const ui
                float scale, void* ws, size_t ws_bytes, void* stream) {
   if (!scale_ok(scale) || !mask_ok(mask)) return FA_ERR_ARG;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !st) return FA_ERR_NULL;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!bf16_head_dim(d)) return FA_ERR_HEADDIM;
   if (!shape_ok(B, H, N_q, d) || !shape_ok(B, H_kv, N_k, d) || H_kv < 1 || H % H_kv != 0) return FA_ERR_SHAPE;
   const View vq{q, B, H, N_q, d, st[0]}, vk{k, B, H_kv, N_k, d, st[1]}, vv{v, B, H_kv, N_k, d, st[2]},
       vo{o, B, H, N_q, d, st[3]}, vdo{dO, B, H, N_q, d, st[4]}, vdq{dq, B, H, N_q, d, st[5]},

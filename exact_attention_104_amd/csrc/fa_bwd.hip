@@ -82,7 +82,13 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
             const float* __restrict__ slopes, Strides sq, Strides sk, Strides sv, Strides sdo, Strides sdk,
             Strides sdv) {
   constexpr int KS = D / 16;    // k-steps over d
-  constexpr int DB = D / 32;    // 32-wide d blocks
+  // dK / dV columns per workgroup: all of d up to 128; at d = 256 two
+  // workgroups share a key block, each accumulating one half of the columns
+  // (S and dP, which contract over all of d, are formed by both), so that the
+  // accumulators and the K / V operands still fit in the 256 AGPRs.
+  constexpr int DC = D == 256 ? 128 : D;
+  constexpr int NH = D / DC;    // column halves per key block
+  constexpr int DB = DC / 32;   // 32-wide d blocks of the accumulators
   constexpr int QT = kBQ * D;   // elements of a Q or dO tile
   static_assert(MASK != kMaskCausal, "causal runs as a band");
   constexpr bool BAND = MASK >= kMaskBand, ALIBI = MASK == kMaskBandAlibi;
@@ -106,9 +112,11 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
   // first. The block's keys serve the group's query heads hk * group + g;
   // with split > 1, workgroup si of the key block takes the gs = group / split
   // heads from hk * group + si * gs and leaves fp32 partials.
-  const int wid = xcd_work_id(nkb * BHkv * split);
-  const int unit = wid / nkb;  // (bhk, si)
-  const int kblk = wid % nkb;
+  const int wid = xcd_work_id(nkb * BHkv * split * NH);
+  const int hc = wid % NH;        // column half
+  const int dc0 = hc * DC;        // first dK / dV column of this workgroup
+  const int unit = wid / NH / nkb;  // (bhk, si)
+  const int kblk = (wid / NH) % nkb;
   const int bhk = unit / split, si = unit % split;
   const int Hkv = H / group, gs = group / split;
   const int b = bhk / Hkv, hk = bhk % Hkv;
@@ -139,8 +147,9 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
 
   if (BAND && nsteps == 0) {  // no query sees these keys: dK = dV = 0
     constexpr int CH = D / 8;
-    for (int e = tid; e < kBKC * CH; e += 256) {
-      const int key = kb0 + e / CH, c = (e % CH) * 8;
+    constexpr int CC = DC / 8;
+    for (int e = tid; e < kBKC * CC; e += 256) {
+      const int key = kb0 + e / CC, c = dc0 + (e % CC) * 8;
       if (key >= Nk) continue;
       if (split == 1) {
         *(u32x4*)(dKg + b * sdk.b + hk * sdk.h + (size_t)key * sdk.n + c) = u32x4{0, 0, 0, 0};
@@ -279,7 +288,7 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
   // of S (slot 8 hi + j holds query 16 s2 + 8 (j / 4) + 4 hi + j % 4)
   auto dvdk_part = [&](const uint16_t* sQ, const uint16_t* sO, int s2, int db) __attribute__((always_inline)) {
     const int r0 = 16 * s2 + 4 * hi + (i16 >> 2);
-    const int d = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
+    const int d = dc0 + db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
     const u32x4 bo = tr_pair(sO + toff<D>(r0, d), sO + toff<D>(r0 + 8, d));
     const u32x4 bq = tr_pair(sQ + toff<D>(r0, d), sQ + toff<D>(r0 + 8, d));
     dv[db] = mfma_bf16_32x32x16(as_bf16x8(pP[s2]), as_bf16x8(bo), dv[db]);
@@ -383,7 +392,7 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
   if (split == 1) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int d = db * 32 + l32;
+      const int d = dc0 + db * 32 + l32;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kw0 + 8 * (i / 4) + 4 * hi + (i % 4);
@@ -399,7 +408,7 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
     float* pv = pk + (size_t)BHkv * split * Nk * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const int d = db * 32 + l32;
+      const int d = dc0 + db * 32 + l32;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kw0 + 8 * (i / 4) + 4 * hi + (i % 4);
@@ -462,7 +471,8 @@ static int launch(const BwdArgs& a) {
   const int nkb = bwd_key_blocks(a.Nk);
   static_assert(kBKC == 128, "bwd_key_blocks assumes 128-key blocks");
   const int BHkv = a.B * a.Hkv;
-  hipLaunchKernelGGL((dkdv_kernel<D, MASK>), dim3((unsigned)(nkb * BHkv * a.split)), dim3(256), 0, st, a.q, a.k,
+  hipLaunchKernelGGL((dkdv_kernel<D, MASK>), dim3((unsigned)(nkb * BHkv * a.split * (D == 256 ? 2 : 1))), dim3(256),
+                     0, st, a.q, a.k,
                      a.v, a.dO, a.lse, a.delta, a.dk, a.dv, a.part, BHkv, a.H, a.H / a.Hkv, a.split, a.Nq, a.Nk,
                      nkb, a.scale, a.scale * kLog2e, a.band, a.slopes, a.sq, a.sk, a.sv, a.sdo, a.sdk, a.sdv);
   if (hipGetLastError() != hipSuccess) return 1;
@@ -485,6 +495,9 @@ static int launch_d(const BwdArgs& a) {
   }
 }
 
-int launch_bwd(const BwdArgs& a) { return a.d == 128 ? launch_d<128>(a) : launch_d<64>(a); }
+int launch_bwd(const BwdArgs& a) {
+  if (a.d == 256) return launch_d<256>(a);
+  return a.d == 128 ? launch_d<128>(a) : launch_d<64>(a);
+}
 
 }  // namespace fa

@@ -18,10 +18,15 @@ namespace fa {
 
 namespace {
 
-constexpr int kQNW = 8;    // dq: waves per workgroup
-constexpr int kQBR = kQNW * 32;  // dq: query rows per workgroup
+// dq: waves per workgroup (four at d = 256, where a wave needs more than the
+// 256 registers of two-per-SIMD residency), query rows per workgroup
+template <int D>
+constexpr int kQNWof = D == 256 ? 4 : 8;
+template <int D>
+constexpr int kQBRof = kQNWof<D> * 32;
 constexpr int kQBC = 64;   // dq: keys per tile
-constexpr int kQThreads = kQNW * 64;
+template <int D>
+constexpr int kQThreadsOf = kQNWof<D> * 64;
 
 }  // namespace
 
@@ -31,7 +36,7 @@ using namespace bwd;
 // 0 .. Nk - 1; kMaskBandAlibi adds -slope_h |i + off - j| to the scaled
 // scores; kMaskNone and kMaskCausal keep the fixed arithmetic).
 template <int D, int MASK>
-__global__ void __launch_bounds__(kQThreads, 1)
+__global__ void __launch_bounds__(kQThreadsOf<D>, 1)
 dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
           const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
           uint16_t* __restrict__ dQg, int BH, int H, int group, int Nq, int Nk, int nqb, float scale,
@@ -41,6 +46,7 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
   constexpr int DB = D / 32;
   constexpr int TILE = kQBC * D;
   constexpr bool BAND = MASK >= kMaskBand, CAUSAL = MASK == kMaskCausal, ALIBI = MASK == kMaskBandAlibi;
+  constexpr int kQBR = kQBRof<D>, kQThreads = kQThreadsOf<D>;
 
   __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
@@ -220,8 +226,8 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
 template <int D, int MASK>
 static int launch_dq(const BwdArgs& a) {
   const int BH = a.B * a.H;
-  const int nqb = (a.Nq + kQBR - 1) / kQBR;
-  hipLaunchKernelGGL((dq_kernel<D, MASK>), dim3((unsigned)(nqb * BH)), dim3(kQThreads), 0, (hipStream_t)a.stream,
+  const int nqb = (a.Nq + kQBRof<D> - 1) / kQBRof<D>;
+  hipLaunchKernelGGL((dq_kernel<D, MASK>), dim3((unsigned)(nqb * BH)), dim3(kQThreadsOf<D>), 0, (hipStream_t)a.stream,
                      a.q, a.k, a.v, a.dO, a.lse, a.delta, a.dq, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale,
                      a.scale * kLog2e, a.band, a.slopes, a.sq, a.sk, a.sv, a.sdo, a.sdq);
   return hipGetLastError() == hipSuccess ? 0 : 1;
@@ -237,6 +243,9 @@ static int launch_dq_d(const BwdArgs& a) {
   }
 }
 
-int launch_bwd_dq(const BwdArgs& a) { return a.d == 128 ? launch_dq_d<128>(a) : launch_dq_d<64>(a); }
+int launch_bwd_dq(const BwdArgs& a) {
+  if (a.d == 256) return launch_dq_d<256>(a);
+  return a.d == 128 ? launch_dq_d<128>(a) : launch_dq_d<64>(a);
+}
 
 }  // namespace fa

@@ -13,7 +13,7 @@ namespace bwd {
 // (4 aligned consecutive rows x 64 bytes).
 template <int D>
 __device__ __forceinline__ int swz2(int row) {
-  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+  return D >= 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 template <int D>
 __device__ __forceinline__ int toff(int row, int col) {

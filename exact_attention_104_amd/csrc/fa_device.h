@@ -98,17 +98,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
 
-// XOR swizzles of 16-byte chunks inside an LDS row of a [rows][D] bf16 tile.
+// XOR swizzles of 16-byte chunks inside an LDS row of a [rows][D] bf16 tile
+// (the banks repeat every 256 bytes, i.e. every 16 chunks; rows of D >= 128
+// span whole bank periods, rows of D = 64 half of one).
 // K tile: read as 32 rows x one chunk per 16 lanes -> chunk ^ f(row) spreads
 // 16 consecutive rows over 16 distinct 16-byte bank groups.
 template <int D>
 __device__ __forceinline__ int swz_k(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+  return D >= 128 ? (row & 15) : ((row >> 1) & 7);
 }
 // V tile: read transposed, 4 rows x 4 chunks per 16-lane group.
 template <int D>
 __device__ __forceinline__ int swz_v(int row) {
-  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+  return D >= 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
 }  // namespace fa

@@ -28,18 +28,24 @@ namespace fa {
 
 namespace {
 
-constexpr int kNW = 8;    // wavefronts per workgroup
+// Wavefronts per workgroup: eight (two per SIMD, so that one wave's softmax
+// overlaps another's products) up to d = 128; four at d = 256, where a wave
+// needs more than the 256 registers of two-per-SIMD residency.
+template <int D>
+constexpr int kNWof = D == 256 ? 4 : 8;
 constexpr int kQW = 32;   // query rows per wavefront
-constexpr int kBR = kNW * kQW;
+template <int D>
+constexpr int kBRof = kNWof<D> * kQW;  // query rows per workgroup
+template <int D>
+constexpr int kThreadsOf = kNWof<D> * 64;
 constexpr int kBC = 64;   // keys per tile
-constexpr int kThreads = kNW * 64;
 #ifndef FA_RESCALE_SLACK
 #define FA_RESCALE_SLACK 8.0f
 #endif
 constexpr float kRescaleSlack = FA_RESCALE_SLACK;  // log2 units; P stays <= 256 in bf16
 
 // Direct global->LDS loads of one [64 x D] bf16 tile. Thread `tid` fills the
-// 16-byte LDS chunks n * kThreads + tid of the tile; the source chunk is chosen
+// 16-byte LDS chunks n * kThreadsOf<D> + tid of the tile; the source chunk is chosen
 // so that LDS holds the XOR-swizzled layout. Rows past the end are read from
 // row N-1 (finite values that are masked, or multiplied by P = 0).
 template <int D, bool IS_V>
@@ -47,6 +53,7 @@ __device__ __forceinline__ void load_tile_async(uint16_t* lds_tile, const uint16
                                                 int N, int tid) {
   constexpr int CH = D / 8;
   const int w = tid >> 6;
+  constexpr int kThreads = kThreadsOf<D>;
 #pragma unroll
   for (int n = 0; n < (kBC * CH) / kThreads; ++n) {
     const int e = n * kThreads + tid;  // 16-byte chunk index inside the tile
@@ -73,7 +80,7 @@ __device__ __forceinline__ void wait_loads_and_sync() {
 // score of query i and key j gets -slope_h |i + off - j|. kMaskNone and
 // kMaskCausal are the no-mask and plain causal bands with fixed arithmetic.
 template <int D, int MASK>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kThreadsOf<D>, 1)
 fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
            const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og, float* __restrict__ LSEg,
            int BH, int H, int group, int Nq, int Nk, int nqb, float scale_log2, Band band,
@@ -82,6 +89,7 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   constexpr int DB = D / 32;        // 32-row d blocks of O^T
   constexpr int TILE = kBC * D;     // elements of one K or V tile
   constexpr bool BAND = MASK >= kMaskBand, CAUSAL = MASK == kMaskCausal, ALIBI = MASK == kMaskBandAlibi;
+  constexpr int kBR = kBRof<D>;
 
   // Four separate arrays so that the compiler can tell the buffer being filled
   // by the direct loads from the one being read.
@@ -159,6 +167,7 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   float m = BAND ? -1e30f : -INFINITY, l = 0.f;
 
   // One tile: K(t), V(t) are in (sK, sV); the loads of tile t+1 go to (nK, nV).
+  const int lane_l32 = l32, lane_hi = hi, lane_g = g, lane_i16 = i16;
   auto tile = [&](int t, const uint16_t* sK, const uint16_t* sV, uint16_t* nK, uint16_t* nV) {
     wait_loads_and_sync();  // tile t landed; every wave finished tile t-1
     if (t + 1 < t1) {
@@ -167,6 +176,17 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     }
     if ((BAND && t < wfirst) || t > wlast) return;  // this wave's rows see none of these keys
     const int k0 = t * kBC;
+    // At d = 256 the lane index passes through an empty asm so that the LDS
+    // addresses derived from it are formed here rather than hoisted out of the
+    // tile loop (64 of them would not fit in registers). Not in the ALiBi
+    // instance: there this variant gave wrong results for windowed ALiBi
+    // (the asm is semantically empty; without it the results are right, at
+    // the cost of a few spilled registers).
+    constexpr bool PIN = D == 256 && !ALIBI;
+    int lp = lane;
+    if constexpr (PIN) asm volatile("" : "+v"(lp));
+    const int l32 = PIN ? (lp & 31) : lane_l32, hi = PIN ? (lp >> 5) : lane_hi;
+    const int g = PIN ? (lp >> 4) : lane_g, i16 = PIN ? (lp & 15) : lane_i16;
 
     // ---- S^T = K Q^T: two 32-key blocks (K operands read one k-step ahead)
     f32x16 s[2];
@@ -311,9 +331,9 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
 
 template <int D, int MASK>
 static int launch(const FwdArgs& a) {
-  const int nqb = (a.Nq + kBR - 1) / kBR;
+  const int nqb = (a.Nq + kBRof<D> - 1) / kBRof<D>;
   const int BH = a.B * a.H;
-  const dim3 grid((unsigned)(nqb * BH)), block(kThreads);
+  const dim3 grid((unsigned)(nqb * BH)), block(kThreadsOf<D>);
   hipLaunchKernelGGL((fwd_kernel<D, MASK>), grid, block, 0, (hipStream_t)a.stream,
                      a.q, a.k, a.v, a.o, a.lse, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.band,
                      a.slopes, a.sq, a.sk, a.sv, a.so);
@@ -330,6 +350,9 @@ static int launch_d(const FwdArgs& a) {
   }
 }
 
-int launch_fwd(const FwdArgs& a) { return a.d == 128 ? launch_d<128>(a) : launch_d<64>(a); }
+int launch_fwd(const FwdArgs& a) {
+  if (a.d == 256) return launch_d<256>(a);
+  return a.d == 128 ? launch_d<128>(a) : launch_d<64>(a);
+}
 
 }  // namespace fa

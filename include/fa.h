@@ -22,7 +22,8 @@
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream). All
  *   calls are asynchronous on that stream; a device fault surfaces at the
  *   caller's next synchronisation.
- * - Supported: d in {64, 128}; B, H, N >= 1 with B*H*N*d < 2^40; causal in {0, 1};
+ * - Supported: d in {64, 128, 256} (the fp8 calls: {64, 128}); B, H, N >= 1 with
+ *   B*H*N*d < 2^40; causal in {0, 1};
  *   scale finite and > 0. Causal means query i sees key j iff j <= i.
  * - Arguments are validated before anything is launched. On error nothing is
  *   written and a status below is returned; the library never prints or aborts.
@@ -44,7 +45,7 @@ enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL */
   FA_ERR_SHAPE = 2,     /* B, H or N < 1, the tensor is too large, or H_kv does not divide H */
-  FA_ERR_HEADDIM = 3,   /* d not supported (or rotation requested with d != 128) */
+  FA_ERR_HEADDIM = 3,   /* d not 64, 128 or 256 (fp8: 64 or 128; rotation: 128) */
   FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned, or a stride not a multiple of 8 */
   FA_ERR_WORKSPACE = 5, /* backward workspace NULL, misaligned or too small */
   FA_ERR_DEVICE = 6,    /* no HIP device, or the current device is not gfx950 */

@@ -51,6 +51,7 @@ def test_workspace_bytes():
     assert n == 2 * 16 * 4096 * 4  # fp32 D per row
     assert lib.fa_bwd_workspace_bytes(1, 1, 3, 64) == 256  # rounded to 256 B
     assert lib.fa_bwd_workspace_bytes(1, 1, 3, 96) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 256) == 256
     assert lib.fa_bwd_workspace_bytes(0, 1, 3, 64) == 0
 
 
@@ -81,7 +82,7 @@ def _fwd(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(causal=2), 9), (dict(scale=float("nan")), 9), (dict(scale=0.0), 9), (dict(scale=-1.0), 9),
     (dict(q=None), 1), (dict(lse=None), 1),
-    (dict(d=96), 3), (dict(d=256), 3),
+    (dict(d=96), 3), (dict(d=192), 3), (dict(d=512), 3),
     (dict(B=0), 2), (dict(N=0), 2), (dict(H=-1), 2), (dict(N=(1 << 24) + 1), 2),
     (dict(k=P + 8), 4), (dict(lse=P + 0x400004), 4),
     (dict(o=P), 7), (dict(lse=P + 0x100000 + 64), 7), (dict(o=P + 0x200000 + 0x10), 7),

@@ -1,6 +1,6 @@
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-widened]
 
 One step runs every kernel of the path once on the headline workload
 (B=2, H=16, N=8192, d=128, causal), inputs already resident in HBM:
@@ -13,6 +13,8 @@ attention FLOPs: forward 4 B H N^2 d / 2, backward 2.5x that, fp8 forward as
 forward), the per-kernel breakdown with % of the MI355X dense MFMA peak, the
 roofline of the dominant kernel (timed with HIP events on the stream it runs
 on), and the fp64 CPU oracle timed on a bounded sample of the same workload.
+After the timed steps (and outside them) the widened rows are timed on their
+own shapes and reported under "widened".
 """
 
 from __future__ import annotations
@@ -52,6 +54,20 @@ def fwd_bytes(b, h, n, d, elt=2):
 def bwd_bytes(b, h, n, d):
     # reads Q, K, V, O, dO (bf16) and LSE; writes dQ, dK, dV (bf16); D written once, read once
     return 8.0 * b * h * n * d * 2 + 4.0 * b * h * n * 3
+
+
+def visible_pairs(n_q, n_k, causal, window=(-1, -1)):
+    """Number of (query, key) pairs a mask leaves visible in one head, counted
+    row by row: query i sees keys c - left .. c + right of 0 .. n_k - 1, with
+    c = i + n_k - n_q (right capped at 0 when causal; -1 = unbounded)."""
+    import numpy as np
+    left, right = window
+    c = np.arange(n_q, dtype=np.int64) + (n_k - n_q)
+    lo = np.zeros(n_q, dtype=np.int64) if left < 0 else np.maximum(0, c - left)
+    hi = np.full(n_q, n_k - 1, dtype=np.int64) if right < 0 else np.minimum(n_k - 1, c + right)
+    if causal:
+        hi = np.minimum(hi, c)
+    return int(np.maximum(0, hi - lo + 1).sum())
 
 
 def quant_bytes(b, h, n, d):
@@ -106,6 +122,73 @@ def cpu_baseline(sample_heads: int):
             "seconds": dt}
 
 
+def widened(fa, dev, q, k, v, do, steps=5, warmup=3):
+    """The widened rows (grouped heads, [B, N, H, d] layout, sliding window,
+    ALiBi, cross-attention, d = 64 and 256) on shapes of the headline's size:
+    bf16 forward and backward, each timed with HIP events on the current
+    stream, algorithmic FLOPs = 4 d x (visible pairs) per head (backward 2.5x).
+    """
+    import numpy as np
+    import torch
+
+    import fa_inputs
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    def case(qq, kk, vv, dd, causal=True, window=None, slopes=None, cfg=""):
+        b_, h_, nq, d_ = qq.shape
+        nk = kk.shape[2]
+        o_, l_ = fa.fwd(qq, kk, vv, causal=causal, window=window, alibi_slopes=slopes)
+        need = fa.bwd_workspace_bytes(b_, h_, nq, d_, H_kv=kk.shape[1], causal=causal, N_k=nk,
+                                      window=window)
+        ws_ = torch.empty(need, dtype=torch.uint8, device=dev)
+        tf = timed(lambda: fa.fwd(qq, kk, vv, causal=causal, window=window, alibi_slopes=slopes, out=o_, lse=l_))
+        tb = timed(lambda: fa.bwd(qq, kk, vv, o_, dd, l_, causal=causal, workspace=ws_, window=window,
+                                  alibi_slopes=slopes))
+        flops = 4.0 * d_ * visible_pairs(nq, nk, causal, window if window is not None else (-1, -1)) * b_ * h_
+        ent = {"config": cfg, "fwd_ms": tf, "bwd_ms": tb,
+               "fwd_tflops": flops / (tf * 1e-3) / 1e12, "bwd_tflops": 2.5 * flops / (tb * 1e-3) / 1e12}
+        ent["fwd_frac"] = ent["fwd_tflops"] / PEAK_BF16
+        ent["bwd_frac"] = ent["bwd_tflops"] / PEAK_BF16
+        log("widened %-8s fwd %.3f ms %.0f TFLOP/s, bwd %.3f ms %.0f TFLOP/s"
+            % (cfg.split(":")[0], tf, ent["fwd_tflops"], tb, ent["bwd_tflops"]))
+        return ent
+
+    out = {}
+    hkv = 2
+    kg, vg = k[:, :hkv].contiguous(), v[:, :hkv].contiguous()
+    out["gqa"] = case(q, kg, vg, do, cfg="gqa: B=2 H=16 H_kv=2 N=8192 d=128 causal")
+    qt, kt, vt, dt = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v, do))
+    out["bnhd"] = case(qt, kt, vt, dt, cfg="bnhd: [B, N, H, d] storage, B=2 H=16 N=8192 d=128 causal")
+    del qt, kt, vt, dt
+    out["window"] = case(q, k, v, do, window=(1024, 0),
+                         cfg="window: B=2 H=16 N=8192 d=128 causal, 1024 keys back")
+    slopes = torch.from_numpy(fa_inputs.alibi_slopes(q.shape[1])).to(dev)
+    out["alibi"] = case(q, k, v, do, slopes=slopes, cfg="alibi: B=2 H=16 N=8192 d=128 causal")
+    nq = q.shape[2] // 4
+    out["cross"] = case(q[:, :, -nq:], k, v, do[:, :, -nq:].contiguous(),
+                        cfg="cross: B=2 H=16 N_q=2048 N_k=8192 d=128 causal (last queries on last keys)")
+    for d_ in (64, 256):
+        x = fa_inputs.attention_inputs(1, 16, 8192, d_, seed=7, with_do=True)
+        qd, kd, vd, dd = (torch.from_numpy(x[n]).to(torch.bfloat16).to(dev) for n in ("q", "k", "v", "do"))
+        del x
+        out["d%d" % d_] = case(qd, kd, vd, dd, cfg="d%d: B=1 H=16 N=8192 d=%d causal" % (d_, d_))
+        del qd, kd, vd, dd
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +196,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=12)
+    ap.add_argument("--no-widened", action="store_true",
+                    help="skip the widened rows (GQA, layout, window, ALiBi, cross-attention, d=64/256)")
     ap.add_argument("--only", default=None,
                     help="time only this kernel (fa_fwd, fa_bwd, fa_quant_fp8, fa_fwd_fp8) or 'copy[MiB]', "
                          "a plain device copy (default 256 MiB) used to calibrate rocprofv3 byte counters")
@@ -241,6 +326,10 @@ def main():
         roofline = {"kernel": name, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM,
                     "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None}
 
+    wid = None
+    if not args.no_widened and args.only is None and have_bwd:
+        wid = widened(fa, dev, q, k, v, do)
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on %d heads" % args.cpu_heads)
@@ -267,6 +356,7 @@ def main():
         "breakdown": breakdown,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "widened": wid,
     }
     print(json.dumps(out), flush=True)
 

@@ -122,7 +122,7 @@ def cpu_baseline(sample_heads: int):
             "seconds": dt}
 
 
-def widened(fa, dev, q, k, v, do, steps=5, warmup=3):
+def widened(fa, dev, q, k, v, do, steps=5, warmup=5):
     """The widened rows (grouped heads, [B, N, H, d] layout, sliding window,
     ALiBi, cross-attention, d = 64 and 256) on shapes of the headline's size:
     bf16 forward and backward, each timed with HIP events on the current

@@ -1,6 +1,6 @@
 """Benchmark of the attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-widened]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-widened] [--no-sweep]
 
 One step runs every kernel of the path once on the headline workload
 (B=2, H=16, N=8192, d=128, causal), inputs already resident in HBM:
@@ -14,7 +14,8 @@ forward), the per-kernel breakdown with % of the MI355X dense MFMA peak, the
 roofline of the dominant kernel (timed with HIP events on the stream it runs
 on), and the fp64 CPU oracle timed on a bounded sample of the same workload.
 After the timed steps (and outside them) the widened rows are timed on their
-own shapes and reported under "widened".
+own shapes and reported under "widened", and a sequence-length sweep under
+"sweep".
 """
 
 from __future__ import annotations
@@ -189,6 +190,68 @@ def widened(fa, dev, q, k, v, do, steps=5, warmup=5):
     return out
 
 
+def sweep(fa, dev, steps=10, warmup=5):
+    """Sequence-length sweep at a fixed token count: N = 512 .. 16384 with
+    B = 16384 / N, H = 16, d = 64 and 128, causal and not; forward and backward
+    timed with HIP events (inputs: seeded normal bf16 drawn on the GPU). Points
+    whose forward is HBM-bound (N / 4 FLOP per byte causal, N / 2 not, below
+    the 314.6 FLOP/B ridge) also get a cold-cache forward time, with a 512 MiB
+    write before each call to evict L2 and the memory-side cache."""
+    import numpy as np
+    import torch
+
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ridge = PEAK_BF16 * 1e12 / (PEAK_HBM * 1e9)
+
+    def timed(fn, cold=False):
+        for _ in range(warmup):
+            fn()
+        times = []
+        for _ in range(steps):
+            if cold:
+                flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        return float(np.median(times))
+
+    g = torch.Generator(device=dev)
+    pts = []
+    for d in (64, 128):
+        for n in (512, 1024, 2048, 4096, 8192, 16384):
+            b = 16384 // n
+            g.manual_seed(100 + int(round(math.log2(n))))
+            q, k, v, do = (torch.randn((b, 16, n, d), generator=g, device=dev).to(torch.bfloat16) for _ in range(4))
+            ws = torch.empty(fa.bwd_workspace_bytes(b, 16, n, d), dtype=torch.uint8, device=dev)
+            for causal in (True, False):
+                o, lse = fa.fwd(q, k, v, causal=causal)
+                tf = timed(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse))
+                tb = timed(lambda: fa.bwd(q, k, v, o, do, lse, causal=causal, workspace=ws))
+                fl = fwd_flops(b, 16, n, d, causal)
+                by = fwd_bytes(b, 16, n, d)
+                ent = {"N": n, "B": b, "H": 16, "d": d, "causal": causal,
+                       "fwd_ms": tf, "fwd_tflops": fl / (tf * 1e-3) / 1e12, "fwd_gbps": by / (tf * 1e-3) / 1e9,
+                       "bwd_ms": tb, "bwd_tflops": 2.5 * fl / (tb * 1e-3) / 1e12}
+                ent["fwd_frac"] = ent["fwd_tflops"] / PEAK_BF16
+                ent["bwd_frac"] = ent["bwd_tflops"] / PEAK_BF16
+                ent["fwd_bound"] = "hbm" if fl / by < ridge else "mfma"
+                if ent["fwd_bound"] == "hbm":
+                    tc = timed(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse), cold=True)
+                    ent["fwd_ms_cold"] = tc
+                    ent["fwd_gbps_cold"] = by / (tc * 1e-3) / 1e9
+                    ent["fwd_hbm_frac_cold"] = ent["fwd_gbps_cold"] / PEAK_HBM
+                log("sweep d=%d N=%5d B=%2d causal=%d: fwd %.3f ms %.0f TFLOP/s, bwd %.3f ms %.0f TFLOP/s%s"
+                    % (d, n, b, causal, tf, ent["fwd_tflops"], tb, ent["bwd_tflops"],
+                       (", cold fwd %.0f GB/s" % ent["fwd_gbps_cold"]) if "fwd_gbps_cold" in ent else ""))
+                pts.append(ent)
+            del q, k, v, do, ws, o, lse
+    return pts
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +259,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=12)
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the sequence-length sweep (N = 512 .. 16384 at 16384 tokens, d = 64 / 128)")
     ap.add_argument("--no-widened", action="store_true",
                     help="skip the widened rows (GQA, layout, window, ALiBi, cross-attention, d=64/256)")
     ap.add_argument("--only", default=None,
@@ -329,6 +394,9 @@ def main():
     wid = None
     if not args.no_widened and args.only is None and have_bwd:
         wid = widened(fa, dev, q, k, v, do)
+    swp = None
+    if not args.no_sweep and args.only is None and have_bwd:
+        swp = sweep(fa, dev)
 
     cpu = None
     if not args.no_cpu:
@@ -357,6 +425,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "widened": wid,
+        "sweep": swp,
     }
     print(json.dumps(out), flush=True)
 

@@ -119,10 +119,15 @@ quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __
 }
 
 // 16-byte chunk swizzle of a [64 keys][D bytes] e4m3 tile: conflict-free for
-// 16-lane row reads and for the 8-row transposed byte reads used for V.
+// 16-lane row reads (16 consecutive rows, one chunk: the 8 row pairs take 8
+// distinct chunks) and for the transposed byte reads of V, which at d = 128
+// take two adjacent chunks of rows {0, 2, 8, 10} (+ const) in one pass: with
+// bits 0 and 1 of (row >> 1) swapped those rows map to disjoint chunk pairs
+// (plain (row >> 1) & 7 pairs rows 0 / 2 and 8 / 10 on the same banks).
 template <int D>
 __device__ __forceinline__ int swz8(int row) {
-  return D == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+  const int x = (row >> 1) & 7;
+  return D == 128 ? (((x & 1) << 1) | ((x >> 1) & 1) | (x & 4)) : ((row >> 2) & 3);
 }
 template <int D>
 __device__ __forceinline__ int toff8(int row, int byte) {

@@ -98,6 +98,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
 
+// Maximum of the 32 values of two accumulator blocks as a tree of three-input
+// maxima (v_max3_f32: 16 instructions where pairwise maxima need 31).
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+__device__ __forceinline__ float max_of_32(const f32x16& a, const f32x16& b) {
+  float t[11];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) t[i] = max3f(a[3 * i], a[3 * i + 1], a[3 * i + 2]);
+  t[5] = max3f(a[15], b[0], b[1]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t[6 + i] = max3f(b[2 + 3 * i], b[3 + 3 * i], b[4 + 3 * i]);
+  t[10] = fmaxf(b[14], b[15]);
+  return max3f(max3f(t[0], t[1], t[2]), max3f(t[3], t[4], t[5]), max3f(t[6], t[7], max3f(t[8], t[9], t[10])));
+}
+
 // XOR swizzles of 16-byte chunks inside an LDS row of a [rows][D] bf16 tile
 // (the banks repeat every 256 bytes, i.e. every 16 chunks; rows of D >= 128
 // span whole bank periods, rows of D = 64 half of one).

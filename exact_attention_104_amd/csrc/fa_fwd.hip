@@ -242,11 +242,7 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
           if (BAND ? (key < klo || key > khi) : ((CAUSAL && key > qrow) || key >= Nk)) s[kb][i] = -INFINITY;
         }
     }
-    float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = (kb == 0 ? 2 : 0); i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
+    float mx = max_of_32(s[0], s[1]);
     mx = fmaxf(mx, other_half(mx));
     if constexpr (!ALIBI) mx *= scale_log2;
     // The running max is replaced (and O, l rescaled) only when some row's max

@@ -30,14 +30,14 @@ namespace {
 
 // Wavefronts per workgroup: eight (two per SIMD, so that one wave's softmax
 // overlaps another's products) up to d = 128; four at d = 256, where a wave
-// needs more than the 256 registers of two-per-SIMD residency.
+// needs more than the 256 registers of two-per-SIMD residency. Short key
+// ranges use four-wave workgroups at d <= 128 too (two workgroups per CU,
+// each wave still at two per SIMD), so that one workgroup's loads, prologue
+// and epilogue overlap another's tiles when every workgroup has only a few.
 template <int D>
 constexpr int kNWof = D == 256 ? 4 : 8;
 constexpr int kQW = 32;   // query rows per wavefront
-template <int D>
-constexpr int kBRof = kNWof<D> * kQW;  // query rows per workgroup
-template <int D>
-constexpr int kThreadsOf = kNWof<D> * 64;
+constexpr int kShortKeys = 1024;  // key ranges up to this length use four-wave workgroups
 constexpr int kBC = 64;   // keys per tile
 #ifndef FA_RESCALE_SLACK
 #define FA_RESCALE_SLACK 8.0f
@@ -45,15 +45,15 @@ constexpr int kBC = 64;   // keys per tile
 constexpr float kRescaleSlack = FA_RESCALE_SLACK;  // log2 units; P stays <= 256 in bf16
 
 // Direct global->LDS loads of one [64 x D] bf16 tile. Thread `tid` fills the
-// 16-byte LDS chunks n * kThreadsOf<D> + tid of the tile; the source chunk is chosen
+// 16-byte LDS chunks n * 64 NW + tid of the tile; the source chunk is chosen
 // so that LDS holds the XOR-swizzled layout. Rows past the end are read from
 // row N-1 (finite values that are masked, or multiplied by P = 0).
-template <int D, bool IS_V>
+template <int D, bool IS_V, int NW>
 __device__ __forceinline__ void load_tile_async(uint16_t* lds_tile, const uint16_t* head, long long rs, int k0,
                                                 int N, int tid) {
   constexpr int CH = D / 8;
   const int w = tid >> 6;
-  constexpr int kThreads = kThreadsOf<D>;
+  constexpr int kThreads = NW * 64;
 #pragma unroll
   for (int n = 0; n < (kBC * CH) / kThreads; ++n) {
     const int e = n * kThreads + tid;  // 16-byte chunk index inside the tile
@@ -79,8 +79,8 @@ __device__ __forceinline__ void wait_loads_and_sync() {
 // are masked element by element. With ALiBi (kMaskBandAlibi) the scaled
 // score of query i and key j gets -slope_h |i + off - j|. kMaskNone and
 // kMaskCausal are the no-mask and plain causal bands with fixed arithmetic.
-template <int D, int MASK>
-__global__ void __launch_bounds__(kThreadsOf<D>, 1)
+template <int D, int MASK, int NW>
+__global__ void __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1)
 fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
            const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og, float* __restrict__ LSEg,
            int BH, int H, int group, int Nq, int Nk, int nqb, float scale_log2, Band band,
@@ -89,7 +89,7 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   constexpr int DB = D / 32;        // 32-row d blocks of O^T
   constexpr int TILE = kBC * D;     // elements of one K or V tile
   constexpr bool BAND = MASK >= kMaskBand, CAUSAL = MASK == kMaskCausal, ALIBI = MASK == kMaskBandAlibi;
-  constexpr int kBR = kBRof<D>;
+  constexpr int kBR = NW * kQW;  // query rows per workgroup
 
   // Four separate arrays so that the compiler can tell the buffer being filled
   // by the direct loads from the one being read.
@@ -145,8 +145,8 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   if constexpr (ALIBI) nslope = -slopes[h] * kLog2e;
 
   if (t1 > t0) {
-    load_tile_async<D, false>(sK0, Kh, sk.n, t0 * kBC, Nk, tid);
-    load_tile_async<D, true>(sV0, Vh, sv.n, t0 * kBC, Nk, tid);
+    load_tile_async<D, false, NW>(sK0, Kh, sk.n, t0 * kBC, Nk, tid);
+    load_tile_async<D, true, NW>(sV0, Vh, sv.n, t0 * kBC, Nk, tid);
   }
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[q][16 ks + 8 hi .. +7].
@@ -171,8 +171,8 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   auto tile = [&](int t, const uint16_t* sK, const uint16_t* sV, uint16_t* nK, uint16_t* nV) {
     wait_loads_and_sync();  // tile t landed; every wave finished tile t-1
     if (t + 1 < t1) {
-      load_tile_async<D, false>(nK, Kh, sk.n, (t + 1) * kBC, Nk, tid);
-      load_tile_async<D, true>(nV, Vh, sv.n, (t + 1) * kBC, Nk, tid);
+      load_tile_async<D, false, NW>(nK, Kh, sk.n, (t + 1) * kBC, Nk, tid);
+      load_tile_async<D, true, NW>(nV, Vh, sv.n, (t + 1) * kBC, Nk, tid);
     }
     if ((BAND && t < wfirst) || t > wlast) return;  // this wave's rows see none of these keys
     const int k0 = t * kBC;
@@ -325,15 +325,24 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   }
 }
 
-template <int D, int MASK>
-static int launch(const FwdArgs& a) {
-  const int nqb = (a.Nq + kBRof<D> - 1) / kBRof<D>;
+template <int D, int MASK, int NW>
+static int launch_nw(const FwdArgs& a) {
+  constexpr int kBR = NW * kQW;
+  const int nqb = (a.Nq + kBR - 1) / kBR;
   const int BH = a.B * a.H;
-  const dim3 grid((unsigned)(nqb * BH)), block(kThreadsOf<D>);
-  hipLaunchKernelGGL((fwd_kernel<D, MASK>), grid, block, 0, (hipStream_t)a.stream,
+  const dim3 grid((unsigned)(nqb * BH)), block(NW * 64);
+  hipLaunchKernelGGL((fwd_kernel<D, MASK, NW>), grid, block, 0, (hipStream_t)a.stream,
                      a.q, a.k, a.v, a.o, a.lse, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.band,
                      a.slopes, a.sq, a.sk, a.sv, a.so);
   return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+template <int D, int MASK>
+static int launch(const FwdArgs& a) {
+  if constexpr (kNWof<D> == 8) {
+    if (a.Nk <= kShortKeys) return launch_nw<D, MASK, 4>(a);
+  }
+  return launch_nw<D, MASK, kNWof<D>>(a);
 }
 
 template <int D>

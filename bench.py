@@ -266,7 +266,16 @@ def main():
     ap.add_argument("--only", default=None,
                     help="time only this kernel (fa_fwd, fa_bwd, fa_quant_fp8, fa_fwd_fp8) or 'copy[MiB]', "
                          "a plain device copy (default 256 MiB) used to calibrate rocprofv3 byte counters")
+    ap.add_argument("--seq", type=int, default=None,
+                    help="with --only: run the timed kernel at sequence length SEQ and batch 16384 // SEQ "
+                         "(the sweep's token count) instead of the headline shape, for profiling the short, "
+                         "bandwidth-bound shapes")
     args = ap.parse_args()
+    if args.seq is not None:
+        if args.only is None or args.only.startswith("copy"):
+            ap.error("--seq profiles one kernel: give --only fa_fwd, fa_bwd, fa_quant_fp8 or fa_fwd_fp8")
+        global B, N
+        N, B = args.seq, max(1, 16384 // args.seq)
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
               "(the (batch, head) pairs would shard with no communication)", file=sys.stderr)
@@ -417,8 +426,8 @@ def main():
         "vs_baseline": None,
         "dtype": "+".join(dtypes),
         "data": "synthetic",
-        "config": {"workload": "causal attention B=2 H=16 N=8192 d=128 (bf16; fp8 leg with 0.1% x20 "
-                               "outliers, Hadamard-rotated Q/K)",
+        "config": {"workload": "causal attention B=%d H=%d N=%d d=%d (bf16; fp8 leg with 0.1%% x20 "
+                               "outliers, Hadamard-rotated Q/K)" % (B, H, N, D),
                    "B": B, "H": H, "N": N, "d": D, "causal": True,
                    "step": [k[0] for k in kernels]},
         "breakdown": breakdown,

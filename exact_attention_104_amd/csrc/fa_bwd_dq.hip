@@ -22,11 +22,15 @@ namespace {
 // 256 registers of two-per-SIMD residency), query rows per workgroup
 template <int D>
 constexpr int kQNWof = D == 256 ? 4 : 8;
-template <int D>
-constexpr int kQBRof = kQNWof<D> * 32;
 constexpr int kQBC = 64;   // dq: keys per tile
-template <int D>
-constexpr int kQThreadsOf = kQNWof<D> * 64;
+// Shorter key ranges use four-wave workgroups at d <= 128 (two per CU, each
+// wave still at two per SIMD): one workgroup's start and end overlap
+// another's tiles, and causal work splits more evenly. Measured on the whole
+// backward: 3-8% faster up to 2048 keys, 1-3% at 4096 causal, 1-2% slower at
+// 8192. Only the no-mask and causal instances: the general-band instance
+// spills registers at four waves.
+constexpr int kQShortKeys = 1024;        // four-wave workgroups up to this many keys without a mask,
+constexpr int kQShortKeysCausal = 4096;  // and up to this many under the causal mask
 
 }  // namespace
 
@@ -35,8 +39,8 @@ using namespace bwd;
 // Masks as in the forward (the band of keys i + off - wl .. i + off + wr of
 // 0 .. Nk - 1; kMaskBandAlibi adds -slope_h |i + off - j| to the scaled
 // scores; kMaskNone and kMaskCausal keep the fixed arithmetic).
-template <int D, int MASK>
-__global__ void __launch_bounds__(kQThreadsOf<D>, 1)
+template <int D, int MASK, int NW>
+__global__ void __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1)
 dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
           const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
           uint16_t* __restrict__ dQg, int BH, int H, int group, int Nq, int Nk, int nqb, float scale,
@@ -46,7 +50,7 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
   constexpr int DB = D / 32;
   constexpr int TILE = kQBC * D;
   constexpr bool BAND = MASK >= kMaskBand, CAUSAL = MASK == kMaskCausal, ALIBI = MASK == kMaskBandAlibi;
-  constexpr int kQBR = kQBRof<D>, kQThreads = kQThreadsOf<D>;
+  constexpr int kQBR = NW * 32, kQThreads = NW * 64;
 
   __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
@@ -226,14 +230,22 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
   }
 }
 
-template <int D, int MASK>
-static int launch_dq(const BwdArgs& a) {
+template <int D, int MASK, int NW>
+static int launch_dq_nw(const BwdArgs& a) {
   const int BH = a.B * a.H;
-  const int nqb = (a.Nq + kQBRof<D> - 1) / kQBRof<D>;
-  hipLaunchKernelGGL((dq_kernel<D, MASK>), dim3((unsigned)(nqb * BH)), dim3(kQThreadsOf<D>), 0, (hipStream_t)a.stream,
+  const int nqb = (a.Nq + NW * 32 - 1) / (NW * 32);
+  hipLaunchKernelGGL((dq_kernel<D, MASK, NW>), dim3((unsigned)(nqb * BH)), dim3(NW * 64), 0, (hipStream_t)a.stream,
                      a.q, a.k, a.v, a.dO, a.lse, a.delta, a.dq, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale,
                      a.scale * kLog2e, a.band, a.slopes, a.sq, a.sk, a.sv, a.sdo, a.sdq);
   return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+template <int D, int MASK>
+static int launch_dq(const BwdArgs& a) {
+  if constexpr (kQNWof<D> == 8 && MASK <= kMaskCausal) {
+    if (a.Nk <= (MASK == kMaskNone ? kQShortKeys : kQShortKeysCausal)) return launch_dq_nw<D, MASK, 4>(a);
+  }
+  return launch_dq_nw<D, MASK, kQNWof<D>>(a);
 }
 
 template <int D>

@@ -30,14 +30,19 @@ namespace {
 
 // Wavefronts per workgroup: eight (two per SIMD, so that one wave's softmax
 // overlaps another's products) up to d = 128; four at d = 256, where a wave
-// needs more than the 256 registers of two-per-SIMD residency. Short key
-// ranges use four-wave workgroups at d <= 128 too (two workgroups per CU,
-// each wave still at two per SIMD), so that one workgroup's loads, prologue
-// and epilogue overlap another's tiles when every workgroup has only a few.
+// needs more than the 256 registers of two-per-SIMD residency. At d <= 128
+// shorter key ranges use four-wave workgroups too (two workgroups per CU,
+// each wave still at two per SIMD): when every workgroup has only a few
+// tiles, one workgroup's loads, prologue and epilogue overlap another's
+// tiles, and under a mask the smaller Q-blocks split the uneven work more
+// evenly. Measured: faster up to 1024 keys without a mask and up to 4096
+// with one; slower beyond (the eight-wave blocks read each K/V tile from
+// HBM or L2 for twice as many rows).
 template <int D>
 constexpr int kNWof = D == 256 ? 4 : 8;
 constexpr int kQW = 32;   // query rows per wavefront
-constexpr int kShortKeys = 1024;  // key ranges up to this length use four-wave workgroups
+constexpr int kShortKeys = 1024;        // four-wave workgroups up to this many keys without a mask,
+constexpr int kShortKeysMasked = 4096;  // and up to this many under a mask
 constexpr int kBC = 64;   // keys per tile
 #ifndef FA_RESCALE_SLACK
 #define FA_RESCALE_SLACK 8.0f
@@ -340,7 +345,7 @@ static int launch_nw(const FwdArgs& a) {
 template <int D, int MASK>
 static int launch(const FwdArgs& a) {
   if constexpr (kNWof<D> == 8) {
-    if (a.Nk <= kShortKeys) return launch_nw<D, MASK, 4>(a);
+    if (a.Nk <= (MASK == kMaskNone ? kShortKeys : kShortKeysMasked)) return launch_nw<D, MASK, 4>(a);
   }
   return launch_nw<D, MASK, kNWof<D>>(a);
 }

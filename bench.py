@@ -375,7 +375,7 @@ def main():
     for i, (name, _, flops, nbytes, peak) in enumerate(kernels):
         times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
         avg = float(np.mean(times))
-        ent = {"ms_avg": avg, "ms_min": float(np.min(times))}
+        ent = {"ms_avg": avg, "ms_median": float(np.median(times)), "ms_min": float(np.min(times))}
         if flops:
             ent["tflops"] = flops / (avg * 1e-3) / 1e12
             ent["pct_of_peak"] = 100.0 * ent["tflops"] / peak
@@ -399,6 +399,28 @@ def main():
         achieved = breakdown[name]["gbps"]
         roofline = {"kernel": name, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM,
                     "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None}
+
+    # Context, outside the timed step: the rate of a large bf16 GEMM from the
+    # vendor library on this machine, a practical ceiling for dense bf16 MFMA work.
+    gemm = None
+    if args.only is None:
+        a_ = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        b_ = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a_, b_)
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(10):
+            torch.matmul(a_, b_)
+        g1.record(stream)
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / 10
+        gemm = {"what": "torch.matmul bf16 8192x8192x8192 (hipBLASLt), 10 calls after 3 warm-ups",
+                "ms": gms, "tflops": 2.0 * 8192 ** 3 / (gms * 1e-3) / 1e12,
+                "frac_of_peak": 2.0 * 8192 ** 3 / (gms * 1e-3) / 1e12 / PEAK_BF16}
+        del a_, b_
 
     wid = None
     if not args.no_widened and args.only is None and have_bwd:
@@ -433,6 +455,7 @@ def main():
         "breakdown": breakdown,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "context": {"library_bf16_gemm": gemm},
         "widened": wid,
         "sweep": swp,
     }

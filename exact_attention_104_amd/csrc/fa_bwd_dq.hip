@@ -52,10 +52,13 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
   constexpr bool BAND = MASK >= kMaskBand, CAUSAL = MASK == kMaskCausal, ALIBI = MASK == kMaskBandAlibi;
   constexpr int kQBR = NW * 32, kQThreads = NW * 64;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK0[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sK1[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV1[TILE];
+  // K(t) and V(t) tiles, double-buffered, in one array so that each V tile
+  // sits a fixed 2 TILE elements after its K tile (one address serves both).
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[4 * TILE];
+  uint16_t* const sK0 = sKV;
+  uint16_t* const sK1 = sKV + TILE;
+  uint16_t* const sV0 = sKV + 2 * TILE;
+  uint16_t* const sV1 = sKV + 3 * TILE;
 
   const int tid = threadIdx.x;
   // The wave index is uniform. Under a general band, readfirstlane lets the
@@ -63,7 +66,6 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
   // masks schedule better without it.
   const int lane = tid & 63, w = BAND ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6, l32 = lane & 31,
             hi = lane >> 5;
-  const int g = lane >> 4, i16 = lane & 15;
 
   const int wid = xcd_work_id(nqb * BH);
   const int bh = wid / nqb;
@@ -123,8 +125,25 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
 
-  auto tile = [&](int t, const uint16_t* sK, const uint16_t* sV, auto masked_tag) __attribute__((always_inline)) {
+  // LDS byte offsets of this lane's operands inside a tile. The swizzle of
+  // toff<D> only flips bits that depend on the lane, so every operand address
+  // is a tile base plus (lane offset XOR a constant of the loop indices):
+  //   K / V operand (kb, ks): kb 64 D + (pk ^ 32 ks)
+  //   K^T reads (kb, h2, db): (kb 32 + 16 h2) 2 D + (pt ^ 64 db), and for the
+  //   rows 8 further: + 16 D + ((pt ^ 32) ^ 64 db)
+  // (both identical to toff<D> for every lane and index; one instruction per
+  // address instead of re-deriving the swizzle in every tile).
+  auto lane_offsets = [](int ln, uint32_t& pk, uint32_t& pt) __attribute__((always_inline)) {
+    const int l32_ = ln & 31, hi_ = ln >> 5, g_ = ln >> 4, i16_ = ln & 15;
+    pk = 2u * (uint32_t)(l32_ * D + ((hi_ ^ swz2<D>(l32_)) << 3));
+    const int z = 2 * (g_ & 1) + ((i16_ & 3) >> 1);
+    const int wv = z ^ swz2<D>(4 * hi_ + (i16_ >> 2));
+    pt = 2u * (uint32_t)((4 * hi_ + (i16_ >> 2)) * D + 4 * (i16_ & 1) + (wv << 3));
+  };
+
+  auto tile = [&](int t, const uint16_t* sK, auto masked_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    const uint32_t kbase = lds_addr(sK);  // V(t) sits 2 TILE elements after K(t)
     const int k0 = t * kQBC;
     // The lane index passes through an empty asm so that the LDS addresses
     // derived from it are formed inside the tile rather than hoisted out of
@@ -134,17 +153,18 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
     constexpr bool PIN = !(CAUSAL && D <= 128);
     int lp = lane;
     if constexpr (PIN) asm volatile("" : "+v"(lp));
-    const int l32 = lp & 31, hi = lp >> 5, g = lp >> 4, i16 = lp & 15;
+    const int l32 = lp & 31, hi = lp >> 5;
+    uint32_t pk, pt;
+    lane_offsets(lp, pk, pt);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // ---- S^T and dP^T for 32 keys (lane = query)
-      const int r = kb * 32 + l32;
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int col = ks * 16 + hi * 8;
-        const bf16x8 ak = as_bf16x8(*(const u32x4*)(sK + toff<D>(r, col)));
-        const bf16x8 av = as_bf16x8(*(const u32x4*)(sV + toff<D>(r, col)));
+        const uint32_t ka = kbase + kb * 64 * D + (pk ^ (32u * ks));
+        const bf16x8 ak = as_bf16x8(lds_load16(ka));
+        const bf16x8 av = as_bf16x8(lds_load16(ka + 4 * TILE));
         s = mfma_bf16_32x32x16(ak, qf[ks], s);
         dp = mfma_bf16_32x32x16(av, of[ks], dp);
       }
@@ -180,29 +200,32 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
       // ---- dQ^T += K^T dS^T over two 16-key steps (K read transposed)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const int r0 = kb * 32 + 16 * h2 + 4 * hi + (i16 >> 2);
+        const uint32_t rb = kbase + (kb * 32 + 16 * h2) * 2 * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int d = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
-          const u32x4 au = tr_pair(sK + toff<D>(r0, d), sK + toff<D>(r0 + 8, d));
+          const i16x4 t0 = lds_read_tr16_at(rb + (pt ^ (64u * db)));
+          const i16x4 t1 = lds_read_tr16_at(rb + 16 * D + ((pt ^ 32u) ^ (64u * db)));
+          const u32x4 au = {__builtin_bit_cast(u32x2, t0)[0], __builtin_bit_cast(u32x2, t0)[1],
+                            __builtin_bit_cast(u32x2, t1)[0], __builtin_bit_cast(u32x2, t1)[1]};
           acc[db] = mfma_bf16_32x32x16(as_bf16x8(au), as_bf16x8(dsb[h2]), acc[db]);
         }
       }
     }
   };
 
-  // Buffers alternate by tile parity (not unrolled, for the same reason).
-  for (int t = t0; t < t1; ++t) {
-    const bool odd = (t - t0) & 1;
+  // Tile t reads buffer (t - t0) % 2 and loads tile t+1 into the other.
+  // Where registers allow (d = 64, and the causal instance at d = 128), the
+  // loop is unrolled by two so that each buffer's base is a constant that
+  // folds into the LDS instructions' offsets; elsewhere the base is chosen at
+  // run time (one add per address: the unrolled form spills there).
+  auto step = [&](int t, const uint16_t* sK, uint16_t* nK, uint16_t* nV) __attribute__((always_inline)) {
     wait_loads_and_sync();  // tile t landed; every wave finished tile t-1
     if (t + 1 < t1) {
-      load_tile_async<D, kQBC, kQThreads, true>(odd ? sK0 : sK1, Kh, sk.n, (t + 1) * kQBC, Nk, tid);
-      load_tile_async<D, kQBC, kQThreads, true>(odd ? sV0 : sV1, Vh, sv.n, (t + 1) * kQBC, Nk, tid);
+      load_tile_async<D, kQBC, kQThreads, true>(nK, Kh, sk.n, (t + 1) * kQBC, Nk, tid);
+      load_tile_async<D, kQBC, kQThreads, true>(nV, Vh, sv.n, (t + 1) * kQBC, Nk, tid);
     }
-    if ((BAND && t < wfirst) || t > wlast) continue;  // this wave's rows see none of these keys
+    if ((BAND && t < wfirst) || t > wlast) return;  // this wave's rows see none of these keys
     const int k0 = t * kQBC;
-    const uint16_t* sK = odd ? sK1 : sK0;
-    const uint16_t* sV = odd ? sV1 : sV0;
     // mask unless every row of this wave sees the whole tile
     bool masked;
     if constexpr (BAND)
@@ -210,9 +233,22 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
     else
       masked = (CAUSAL && k0 + kQBC - 1 > qw0) || k0 + kQBC > Nk;
     if (masked)
-      tile(t, sK, sV, std::true_type{});
+      tile(t, sK, std::true_type{});
     else
-      tile(t, sK, sV, std::false_type{});
+      tile(t, sK, std::false_type{});
+  };
+  if constexpr (D == 64 || (CAUSAL && D == 128)) {
+    int t = t0;
+    for (; t + 1 < t1; t += 2) {
+      step(t, sK0, sK1, sV1);
+      step(t + 1, sK1, sK0, sV0);
+    }
+    if (t < t1) step(t, sK0, sK1, sV1);
+  } else {
+    for (int t = t0; t < t1; ++t) {
+      const bool odd = (t - t0) & 1;
+      step(t, odd ? sK1 : sK0, odd ? sK0 : sK1, odd ? sV0 : sV1);
+    }
   }
 
   // ---- dQ = scale dQ^T^T, bf16 (lane = query, d over the accumulator rows)

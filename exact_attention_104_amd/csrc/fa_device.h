@@ -74,6 +74,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// LDS reads at a byte address (lds_addr of a __shared__ object plus an offset).
+__device__ __forceinline__ u32x4 lds_load16(uint32_t a) {
+  return *(const __attribute__((address_space(3))) u32x4*)(size_t)a;
+}
+__device__ __forceinline__ i16x4 lds_read_tr16_at(uint32_t a) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(size_t)a);
+}
 __device__ __forceinline__ void lds_dma16(void* lds_wave_base, const void* src) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave_base));
   uint32_t saved;

@@ -168,6 +168,16 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
         s = mfma_bf16_32x32x16(ak, qf[ks], s);
         dp = mfma_bf16_32x32x16(av, of[ks], dp);
       }
+      // issue order: four operand reads ahead of their products
+      if constexpr (D == 64 || (CAUSAL && D == 128)) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * KS - 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
       // ---- dS^T = P^T o (dP^T - D), packed as the B operands of K^T dS^T
       u32x4 dsb[2];
 #pragma unroll

@@ -220,6 +220,16 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
         a[1] = an[1];
       }
     }
+    // issue order: four K operand reads ahead of their products
+    if constexpr (D <= 128 && !BAND) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * KS - 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
     // ---- ALiBi: scores to the exp2 domain with the bias, -slope |i + off - j|
     if constexpr (ALIBI) {
       const float fb = (float)(k0 + 4 * hi - qrow - band.off);  // j - (i + off) of element 0

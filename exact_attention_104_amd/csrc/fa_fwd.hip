@@ -221,7 +221,7 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       }
     }
     // issue order: four K operand reads ahead of their products
-    if constexpr (D <= 128) {
+    {
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int i = 0; i < 2 * KS - 4; ++i) {

@@ -351,7 +351,7 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
     // Issue order (one wave per SIMD, so the order is the overlap): the S / dP
     // products each with up to three LDS reads (their operand and the
     // transposed reads of the dV / dK products, read well ahead of use), then
-    // the dV / dK products with ten vector instructions of P / dS work after
+    // the dV / dK products with seven vector instructions of P / dS work after
     // each.
 #pragma unroll
     for (int i = 0; i < 2 * KS; ++i) {
@@ -362,7 +362,7 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
     for (int i = 0; i < 4 * DB; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);   // VALU
     }
   };
   int nq0 = q_hi;  // query block and head of step j + 1 (after the update below)

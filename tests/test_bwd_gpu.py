@@ -44,6 +44,16 @@ def test_bwd_edge_lengths(gpu, N, d, causal):
     _check_grads([to_host(t) for t in got], ref, "N%d d%d c%d" % (N, d, causal))
 
 
+@pytest.mark.parametrize("N,causal", [(1024, False), (1025, False), (4097, True)])
+def test_bwd_workgroup_shape_boundaries(gpu, N, causal):
+    """The dQ pass on both sides of its switch between four- and eight-wave
+    workgroups (1024 keys without a mask, 4096 causal; 4096 itself is the
+    backward workload below), the longer ones ragged."""
+    host, dev, _, got = _run(gpu, 1, 1, N, 128, causal, 3100 + N)
+    ref = A.backward(host["q"], host["k"], host["v"], host["do"], causal, 1.0 / math.sqrt(128))
+    _check_grads([to_host(t) for t in got], ref, "N%d c%d" % (N, causal))
+
+
 def test_bwd_n4096_d128_causal(gpu):
     """The backward workload: B=2, H=16, N=4096, d=128, causal; O, LSE from fa_fwd."""
     B, H, N, d = 2, 16, 4096, 128

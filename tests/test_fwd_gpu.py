@@ -47,6 +47,14 @@ def test_fwd_edge_lengths(gpu, N, d, causal):
     _full(gpu, 1, 3, N, d, causal, 1000 + N)
 
 
+@pytest.mark.parametrize("N,causal", [(1024, False), (1025, False), (4096, True), (4097, True)])
+def test_fwd_workgroup_shape_boundaries(gpu, N, causal):
+    """Key lengths on both sides of the switch between four- and eight-wave
+    workgroups (1024 keys without a mask, 4096 under the causal mask), the
+    longer ones ragged."""
+    _full(gpu, 1, 2, N, 128, causal, 3000 + N)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_fwd_several_tiles_d(gpu, d):
     _full(gpu, 2, 3, 1000, d, True, 77)

@@ -21,3 +21,16 @@ def test_visible_pairs_headline_shapes():
     w = 1024  # a causal window 1024 keys back: rows 0..1023 see i + 1 keys, the rest 1025
     assert bench.visible_pairs(n, n, True, (w, 0)) == w * (w + 1) // 2 + (n - w) * (w + 1)
     assert bench.visible_pairs(2048, n, True) == sum(i + n - 2048 + 1 for i in range(2048))
+
+
+@pytest.mark.parametrize("args", [["--seq", "512"], ["--seq", "512", "--only", "copy64"], ["--gpus", "2"]])
+def test_bench_refuses_unsupported_runs(args):
+    """--seq profiles one attention kernel (it needs --only with a kernel name), and
+    more than one GPU is refused: both before any GPU work."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py")] + args, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2, (r.returncode, r.stderr[-500:])

@@ -12,13 +12,14 @@
 // then scale = fl32(amax / 448), codes = e4m3(clamp(fl32(x' * fl32(448 / amax)))).
 //
 // Forward: as the bf16 forward (eight split-Q waves of 32 query rows, S^T =
-// K Q^T so lanes own queries, online exp2 softmax with conditional rescale,
+// K Q^T so lanes own queries, online exp2 softmax with threshold rescale,
 // direct global->LDS double-buffered tiles, one barrier per tile), on
 // v_mfma_f32_32x32x64 e4m3 products with fp32 accumulation. Block scales are
 // applied after the products: S = sq * sk * (Q8 K8^T). P is quantised to e4m3
 // for the P V product with the V block scale folded in: p' = p * sv_j * R with
-// R = 256 / max_j sv_j (so p' <= 256), the row sum keeps the unscaled p, and
-// the final division removes R.
+// R = 32 / max_j sv_j, where p is taken against a running max that is moved
+// only when some row's maximum exceeds it by more than 3 (log2 units), so
+// p' <= 256; the row sum keeps the unscaled p, and the final division removes R.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -141,6 +142,7 @@ constexpr int kF8QW = 32;             // query rows per wavefront
 constexpr int kF8BR = kF8NW * kF8QW;  // 256 query rows per workgroup
 constexpr int kF8BC = 64;             // keys per tile
 constexpr int kF8Threads = kF8NW * 64;
+constexpr float kF8Lazy = 3.f;        // rescale threshold (log2 units) of the running max
 
 // Direct global->LDS loads of one [64 x D] e4m3 tile into the swizzled layout
 // of toff8 (rows past the end read row N-1; they are masked or meet P = 0).
@@ -199,12 +201,13 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   load_tile8_async<D>(sK0, Kh, 0, N, tid);
   load_tile8_async<D>(sV0, Vh, 0, N, tid);
 
-  // R = 256 / max_j sv_j over the head, so every quantised p' = p sv_j R <= 256
+  // R = 32 / max_j sv_j over the head: with the running max at most kF8Lazy
+  // below a row's true maximum, every quantised p' = p sv_j R <= 32 * 8 = 256
   float svm = 0.f;
   for (int i = lane; i < nsb; i += 64) svm = fmaxf(svm, vs_h[i]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) svm = fmaxf(svm, __shfl_xor(svm, o));
-  const float R = 256.f / svm;
+  const float R = 32.f / svm;
   const float sq = qs_h[min(qw0, N - 1) / 128];  // the wave's 32 rows share one scale block
 
   // Q8 as the B operand of S^T = K Q^T: lane holds Q8[q][64 ks + 32 hi .. +31]
@@ -264,16 +267,18 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
         }
     }
     float mx = max_of_32(s[0], s[1]);
-    mx = fmaxf(mx, other_half(mx));
-    const float m_new = fmaxf(m, mx * ct);
-    if (__any(m_new > m)) {
+    mx = fmaxf(mx, other_half(mx)) * ct;
+    // lazy rescale: the running max moves only once some row's tile maximum
+    // exceeds it by more than kF8Lazy (log2 units)
+    if (__any(mx > m + kF8Lazy)) {
+      const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      m = m_new;
     }
-    m = m_new;
-    const float off = tt - m_new;
+    const float off = tt - m;
     float rs = 0.f;
     i32x8 pb;
 #pragma unroll
@@ -286,8 +291,8 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
           p[e] = fast_exp2(__builtin_fmaf(s[kb][4 * q4 + e], ct, off));
           rs += p[e];
         }
-        // no clamp needed: m_new >= this tile's scaled maximum, so p' <= ft <=
-        // 256 (up to rounding), inside the e4m3 range of +-448
+        // no clamp needed: m >= this tile's scaled maximum - kF8Lazy, so
+        // p' <= 8 ft <= 256 (up to rounding), inside the e4m3 range of +-448
         pb[kb * 4 + q4] = (int)pack_e4m3x4(p[0], p[1], p[2], p[3]);
       }
     }

@@ -142,6 +142,38 @@ def test_fwd_fp8_n8192_sampled(gpu, rot):
     assert max(errs) <= FP8_O_REL_RMS
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_fp8_rising_scores(gpu, causal):
+    """Scores that grow along the keys (about 1.3 in log2 units per 64-key
+    tile), so the running max lags each row's maximum by up to the rescale
+    threshold and the quantised p' come close to their bound, and one key far
+    above the trend that forces a large rescale late in the row."""
+    B, H, N, d = 1, 2, 1024, 128
+    rng = np.random.default_rng(41)
+    t = 1.27 * np.arange(N) / N
+    t[900] = 2.5
+    q = np.ones((B, H, N, d)) + 0.1 * rng.standard_normal((B, H, N, d))
+    k = t[None, None, :, None] * np.ones((B, H, N, d)) + 0.1 * rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    dev = {n: torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda() for n, x in (("q", q), ("k", k), ("v", v))}
+    qz = _quant_all(gpu, None, dev, False)
+    o, lse = gpu.fwd_fp8(qz["q"][0], qz["k"][0], qz["v"][0], qz["q"][1], qz["k"][1], qz["v"][1], causal=causal)
+    torch.cuda.synchronize()
+    deq = {n: F.dequantize(qz[n][0].cpu().numpy(), qz[n][1].cpu().numpy()) for n in ("q", "k", "v")}
+    o, lse = to_host(o), to_host(lse)
+    scale = 1.0 / math.sqrt(d)
+    o_ref, lse_ref = A.forward(deq["q"], deq["k"], deq["v"], causal, scale)
+    span = (lse_ref[..., -1] - lse_ref[..., 0]) / math.log(2)
+    e = A.rel_rms(o, o_ref)
+    print("fp8 rising c%d: LSE span %.1f (log2) rel_rms=%.3e lse=%.2e" % (causal, span.min(), e, A.max_abs(lse, lse_ref)),
+          flush=True)
+    assert causal == 0 or span.min() > 15  # the rows' maxima do travel well past the threshold
+    assert np.isfinite(o).all() and e <= FP8_O_REL_RMS
+    for h in range(H):
+        bnd = lse_bound(deq["q"][0, h], deq["k"][0, h], scale, causal)
+        assert np.all(np.abs(lse[0, h] - lse_ref[0, h]) <= bnd)
+
+
 def test_quant_bit_exact_n8192(gpu):
     host, dev = inputs_on_device(2, 16, 8192, 128, 5, outliers=True)
     _assert_quant_bit_exact(host, _quant_all(gpu, host, dev, True), "n8192 rot")

@@ -34,6 +34,33 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return (uint32_t)r;
 }
 
+// Value of x held by lane (lane ^ M) of the same 16-lane row, M in {1, 2, 4, 8},
+// moved with DPP lane selects on the vector ALU (no LDS crossbar traffic):
+// quad_perm [1,0,3,2] and [2,3,0,1] for 1 and 2; for 4 the half-row mirror
+// (j -> j ^ 7 within 8 lanes) followed by quad_perm [3,2,1,0] (j -> j ^ 3);
+// for 8 a rotation of the row by 8 lanes.
+template <int M>
+__device__ __forceinline__ float row16_xor(float x) {
+  const int v = __builtin_bit_cast(int, x);
+  int r;
+  if constexpr (M == 1) r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (M == 2) r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (M == 4) r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false), 0x1B, 0xF, 0xF, false);
+  else r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
+  return __builtin_bit_cast(float, r);
+}
+
+// One butterfly stage across lanes c and c ^ M of a row: the lower lane keeps
+// the sum, the upper the difference (partner minus own value), both as
+// fma(x, +-1, partner): x * (+-1) is exact, so each is the one rounding of
+// x + partner or partner - x.
+template <int M>
+__device__ __forceinline__ void lane_butterfly(float (&x)[8], int c) {
+  const float sgn = (c & M) == 0 ? 1.f : -1.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(x[i], sgn, row16_xor<M>(x[i]));
+}
+
 template <int D, bool ROT>
 __global__ void __launch_bounds__(256)
 quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __restrict__ scales,
@@ -48,10 +75,12 @@ quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __
   const int tid = threadIdx.x, c = tid % LPR, rr = tid / LPR;
   const size_t base = bh * (size_t)N * D;
 
-  bool neg[8];
+  // the random signs as sign-bit masks of the packed bf16 pairs (bits 15, 31)
+  uint32_t smask[4] = {0, 0, 0, 0};
   if (ROT) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) neg[j] = signs[c * 8 + j] < 0;
+    for (int j = 0; j < 4; ++j)
+      smask[j] = (signs[c * 8 + 2 * j] < 0 ? 0x8000u : 0u) | (signs[c * 8 + 2 * j + 1] < 0 ? 0x80000000u : 0u);
   }
   float x[PASSES][8];
   float amax = 0.f;
@@ -60,14 +89,16 @@ quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __
     const int row = blk * 128 + p * RPP + rr;
     u32x4 u = {0, 0, 0, 0};
     if (row < N) u = *(const u32x4*)(X + base + (size_t)row * D + c * 8);
+    if (ROT) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u[j] ^= smask[j];  // s o x: negation is a sign-bit flip
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       x[p][2 * j] = __builtin_bit_cast(float, u[j] << 16);
       x[p][2 * j + 1] = __builtin_bit_cast(float, u[j] & 0xffff0000u);
     }
     if (ROT) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[p][j] = neg[j] ? -x[p][j] : x[p][j];
       // strides 1, 2, 4 inside the lane
 #pragma unroll
       for (int h = 1; h < 8; h *= 2)
@@ -79,15 +110,11 @@ quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __
             x[p][i + h] = a - b;
           }
       // strides 8, 16, 32, 64 across the row's 16 lanes
-#pragma unroll
-      for (int m = 1; m < LPR; m *= 2) {
-        const bool lower = (c & m) == 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float o = __shfl_xor(x[p][i], m);
-          x[p][i] = lower ? x[p][i] + o : o - x[p][i];
-        }
-      }
+      static_assert(!ROT || LPR == 16, "the rotation is defined for d = 128");
+      lane_butterfly<1>(x[p], c);
+      lane_butterfly<2>(x[p], c);
+      lane_butterfly<4>(x[p], c);
+      lane_butterfly<8>(x[p], c);
       const float inv_sqrt128 = 0x1.6a09e6p-4f;  // fl32(1 / sqrt(128))
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[p][i] = x[p][i] * inv_sqrt128;

@@ -164,32 +164,36 @@ __device__ __forceinline__ int toff8(int row, int byte) {
 
 namespace {
 
-constexpr int kF8NW = 8;              // wavefronts per workgroup
+// Workgroups of NW wavefronts (8: 256 query rows, one per CU; 4: 128 rows,
+// two per CU, which balance short and causal rows better).
 constexpr int kF8QW = 32;             // query rows per wavefront
-constexpr int kF8BR = kF8NW * kF8QW;  // 256 query rows per workgroup
 constexpr int kF8BC = 64;             // keys per tile
-constexpr int kF8Threads = kF8NW * 64;
 constexpr float kF8Lazy = 3.f;        // rescale threshold (log2 units) of the running max
 
 // Direct global->LDS loads of one [64 x D] e4m3 tile into the swizzled layout
-// of toff8 (rows past the end read row N-1; they are masked or meet P = 0).
-template <int D>
+// of toff8 (rows past the end read row N-1; they are masked or meet P = 0),
+// 16-byte chunk i by thread i mod (64 NW), whole wavefronts at a time.
+template <int D, int NW>
 __device__ __forceinline__ void load_tile8_async(uint8_t* lds_tile, const uint8_t* head, int k0, int N, int tid) {
   constexpr int CHB = D / 16;
   constexpr int CHUNKS = kF8BC * CHB;  // 512 (D = 128) or 256 (D = 64)
-  if (CHUNKS < kF8Threads && tid >= CHUNKS) return;
-  const int w = tid >> 6;
-  const int r = tid / CHB, p = tid % CHB;
-  const int c = p ^ swz8<D>(r);
-  const int row = min(k0 + r, N - 1);
-  const uint8_t* src = head + (size_t)row * D + c * 16;
-  lds_dma16(lds_tile + w * 64 * 16, src);  // lane l lands at +16 l bytes
+  constexpr int T = NW * 64;
+#pragma unroll
+  for (int i0 = 0; i0 < CHUNKS; i0 += T) {
+    const int i = i0 + tid;
+    if (CHUNKS - i0 < T && i >= CHUNKS) return;  // whole wavefronts (CHUNKS is a multiple of 64)
+    const int r = i / CHB, p = i % CHB;
+    const int c = p ^ swz8<D>(r);
+    const int row = min(k0 + r, N - 1);
+    const uint8_t* src = head + (size_t)row * D + c * 16;
+    lds_dma16(lds_tile + (i - (tid & 63)) * 16, src);  // lane l lands at +16 l bytes
+  }
 }
 
 }  // namespace
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kF8Threads, 1)
+template <int D, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
                const float* __restrict__ QS, const float* __restrict__ KSc, const float* __restrict__ VS,
                uint16_t* __restrict__ Og, float* __restrict__ LSEg, int BH, int N, int nqb, int nsb,
@@ -215,18 +219,19 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint8_t* Kh = K8 + head;
   const uint8_t* Vh = V8 + head;
-  const int qw0 = qblk * kF8BR + w * kF8QW;
+  constexpr int BR = NW * kF8QW;  // query rows per workgroup
+  const int qw0 = qblk * BR + w * kF8QW;
   const int qrow = qw0 + l32;
   const float* qs_h = QS + (size_t)bh * nsb;
   const float* ks_h = KSc + (size_t)bh * nsb;
   const float* vs_h = VS + (size_t)bh * nsb;
 
-  const int kend = CAUSAL ? min(N, qblk * kF8BR + kF8BR) : N;
+  const int kend = CAUSAL ? min(N, qblk * BR + BR) : N;
   const int ntiles = (kend + kF8BC - 1) / kF8BC;
   const int wlast = CAUSAL ? min(ntiles - 1, (qw0 + kF8QW - 1) / kF8BC) : ntiles - 1;
 
-  load_tile8_async<D>(sK0, Kh, 0, N, tid);
-  load_tile8_async<D>(sV0, Vh, 0, N, tid);
+  load_tile8_async<D, NW>(sK0, Kh, 0, N, tid);
+  load_tile8_async<D, NW>(sV0, Vh, 0, N, tid);
 
   // R = 32 / max_j sv_j over the head: with the running max at most kF8Lazy
   // below a row's true maximum, every quantised p' = p sv_j R <= 32 * 8 = 256
@@ -352,8 +357,8 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
     wait_vmem_all();
     __syncthreads();  // tile t landed; every wave finished tile t-1
     if (!LAST && t + 1 < ntiles) {
-      load_tile8_async<D>(nK, Kh, (t + 1) * kF8BC, N, tid);
-      load_tile8_async<D>(nV, Vh, (t + 1) * kF8BC, N, tid);
+      load_tile8_async<D, NW>(nK, Kh, (t + 1) * kF8BC, N, tid);
+      load_tile8_async<D, NW>(nV, Vh, (t + 1) * kF8BC, N, tid);
     }
     if (t > wlast) return;
     const int k0 = t * kF8BC;
@@ -411,14 +416,27 @@ int launch_quant_fp8(const QuantArgs& a) {
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-template <int D, bool CAUSAL>
-static int launch_f8(const Fp8FwdArgs& a) {
-  const int nqb = (a.N + kF8BR - 1) / kF8BR, nsb = (a.N + 127) / 128;
+template <int D, bool CAUSAL, int NW>
+static int launch_f8_nw(const Fp8FwdArgs& a) {
+  constexpr int BR = NW * kF8QW;
+  const int nqb = (a.N + BR - 1) / BR, nsb = (a.N + 127) / 128;
   const int BH = a.B * a.H;
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3((unsigned)(nqb * BH)), dim3(kF8Threads), 0,
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, NW>), dim3((unsigned)(nqb * BH)), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, a.q8, a.k8, a.v8, a.qs, a.ks, a.vs, a.o, a.lse, BH, a.N, nqb,
                      nsb, a.scale * kLog2e);
   return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// Four-wave workgroups (two per CU) were faster for every causal length and
+// at d = 64 (2-24%), and for non-causal d = 128 up to N = 2048; above that
+// the eight-wave workgroup was 2-4% faster.
+constexpr int kF8WideKeys = 2048;
+template <int D, bool CAUSAL>
+static int launch_f8(const Fp8FwdArgs& a) {
+  if constexpr (D == 128 && !CAUSAL) {
+    if (a.N > kF8WideKeys) return launch_f8_nw<D, CAUSAL, 8>(a);
+  }
+  return launch_f8_nw<D, CAUSAL, 4>(a);
 }
 
 int launch_fwd_fp8(const Fp8FwdArgs& a) {

@@ -119,6 +119,22 @@ def test_fwd_fp8_kernel_parity(gpu, N, causal, d, rot):
     assert np.all(np.abs(lse - lse_ref) <= bnd), "LSE outside the MFMA accumulation bound"
 
 
+@pytest.mark.parametrize("N", [2048, 2049])
+def test_fwd_fp8_workgroup_shape_boundary(gpu, N):
+    """Non-causal d = 128 runs four-wave workgroups up to 2048 keys and
+    eight-wave ones beyond: both sides of the switch, the second with a
+    ragged last query block and key tile."""
+    host, deq, o, lse = _fp8_case(gpu, 1, 2, N, 128, False, True, 90 + N)
+    scale = 1.0 / math.sqrt(128)
+    o_ref, lse_ref = A.forward(deq["q"], deq["k"], deq["v"], False, scale)
+    e = A.rel_rms(o, o_ref)
+    print("fp8 N%d d128 c0 rot1: rel_rms=%.3e lse=%.2e" % (N, e, A.max_abs(lse, lse_ref)), flush=True)
+    assert np.isfinite(o).all() and e <= FP8_O_REL_RMS
+    for h in range(2):
+        bnd = lse_bound(deq["q"][0, h], deq["k"][0, h], scale, False)
+        assert np.all(np.abs(lse[0, h] - lse_ref[0, h]) <= bnd)
+
+
 @pytest.mark.parametrize("rot", [False, True])
 def test_fwd_fp8_n8192_sampled(gpu, rot):
     """The fp8 workload: B=2, H=16, N=8192, d=128, causal, 0.1% x20 outliers;

@@ -11,7 +11,7 @@
 // strides 1, 2, 4 inside a lane's 8 values and 8, 16, 32, 64 across lanes;
 // then scale = fl32(amax / 448), codes = e4m3(clamp(fl32(x' * fl32(448 / amax)))).
 //
-// Forward: as the bf16 forward (eight split-Q waves of 32 query rows, S^T =
+// Forward: as the bf16 forward (split-Q waves of 32 query rows, S^T =
 // K Q^T so lanes own queries, online exp2 softmax with threshold rescale,
 // direct global->LDS double-buffered tiles, one barrier per tile), on
 // v_mfma_f32_32x32x64 e4m3 products with fp32 accumulation. Block scales are

@@ -8,14 +8,18 @@ One step runs every kernel of the path once on the headline workload
   ->  fa_quant_fp8 on Q, K (random-sign Hadamard rotation) and V  ->  fa_fwd_fp8.
 Kernels that are not built yet are left out of the step and listed as such.
 
-Prints ONE JSON line on stdout: whole-step algorithmic TFLOP/s (causal
-attention FLOPs: forward 4 B H N^2 d / 2, backward 2.5x that, fp8 forward as
-forward), the per-kernel breakdown with % of the MI355X dense MFMA peak, the
-roofline of the dominant kernel (timed with HIP events on the stream it runs
-on), and the fp64 CPU oracle timed on a bounded sample of the same workload.
-After the timed steps (and outside them) the widened rows are timed on their
-own shapes and reported under "widened", and a sequence-length sweep under
-"sweep".
+Prints ONE JSON line on stdout. "value" is the metric exactly: the bf16
+forward + backward rate, algorithmic causal FLOPs (forward 4 B H N^2 d / 2,
+backward 2.5x that) over the two calls' own times inside the timed steps (HIP
+events on the stream they run on), with its fraction of the 2516.6 TFLOP/s
+dense bf16 MFMA peak. The fp8 leg (quantiser and e4m3 forward) runs in every
+step too and is reported on its own in "breakdown" (against the 5033.2 TFLOP/s
+e4m3 peak, and HBM for the quantiser). Also: the roofline of the dominant
+kernel, the shader clock sampled from sysfs while the bf16 kernels run (with
+the utilisation normalised to it), and the fp64 CPU oracle timed on a bounded
+sample of the same workload. After the timed steps (and outside them) the
+widened rows are timed on their own shapes ("widened") and a sequence-length
+sweep ("sweep"), each as median / min / max over repeated calls.
 """
 
 from __future__ import annotations
@@ -96,6 +100,93 @@ def measured_traffic(path: str):
         return None
 
 
+def cpu_model() -> str | None:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def call_stats(times):
+    """median / min / max (ms) of repeated calls; the individual times too when
+    the slowest is more than twice the median (a stall, not the kernel)."""
+    import numpy as np
+    t = np.asarray(times, dtype=np.float64)
+    med = float(np.median(t))
+    out = {"ms_median": med, "ms_min": float(t.min()), "ms_max": float(t.max()), "calls": int(t.size)}
+    if t.max() > 2.0 * med:
+        out["ms_each"] = [float(x) for x in t]
+    return out
+
+
+def sclk_file():
+    """The sysfs file that lists the shader clock levels of this GPU (the
+    current one marked '*'), or None."""
+    import glob
+    cands = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not cands:
+        return None
+    try:
+        import torch
+        p = torch.cuda.get_device_properties(0)
+        bus = "%04x:%02x:%02x" % (getattr(p, "pci_domain_id", 0), p.pci_bus_id, p.pci_device_id)
+        for c in cands:
+            if bus in os.path.realpath(os.path.dirname(c)):
+                return c
+    except Exception:
+        pass
+    return cands[0] if len(cands) == 1 else None
+
+
+def read_sclk_mhz(path):
+    try:
+        for line in open(path):
+            if line.strip().endswith("*"):
+                v = line.split(":", 1)[1].strip().rstrip("*").strip().lower()
+                return float(v.replace("mhz", ""))
+    except (OSError, ValueError, IndexError):
+        pass
+    return None
+
+
+def sample_sclk(run, seconds=1.5):
+    """Run `run` (one bf16 forward + backward) back to back for about `seconds`
+    while a thread reads the current shader clock every 10 ms."""
+    import threading
+    import numpy as np
+    import torch
+    path = sclk_file()
+    if path is None:
+        return {"mhz_median": None, "reason": "no pp_dpm_sclk in sysfs for this GPU"}
+    vals, stop = [], threading.Event()
+
+    def reader():
+        while not stop.is_set():
+            v = read_sclk_mhz(path)
+            if v is not None:
+                vals.append(v)
+            time.sleep(0.01)
+
+    th = threading.Thread(target=reader, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(5):
+            run()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not vals:
+        return {"mhz_median": None, "reason": "sysfs clock unreadable", "file": path}
+    v = np.asarray(vals)
+    return {"mhz_median": float(np.median(v)), "mhz_min": float(v.min()), "mhz_max": float(v.max()),
+            "samples": int(v.size), "file": path,
+            "how": "sysfs pp_dpm_sclk current level, every 10 ms while bf16 fa_fwd + fa_bwd run back to back"}
+
+
 def cpu_baseline(sample_heads: int):
     """The fp64 oracle (as it stands) on `sample_heads` heads of the bf16
     workload: one forward and one backward per head."""
@@ -116,14 +207,16 @@ def cpu_baseline(sample_heads: int):
     dt = time.perf_counter() - t0
     flops = 3.5 * fwd_flops(1, sample_heads, N, D)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    cores = len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": min(cores, int(threads)),
+            "host_cores": cores, "blas_threads": int(threads), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": "fp64 forward + backward by definition on %d of the %d heads of the "
                       "B=%d H=%d N=%d d=%d causal workload (%.1f s); algorithmic causal FLOPs / wall time"
                       % (sample_heads, B * H, B, H, N, D, dt),
             "seconds": dt}
 
 
-def widened(fa, dev, q, k, v, do, steps=5, warmup=5):
+def widened(fa, dev, q, k, v, do, steps=10, warmup=5):
     """The widened rows (grouped heads, [B, N, H, d] layout, sliding window,
     ALiBi, cross-attention, d = 64 and 256) on shapes of the headline's size:
     bf16 forward and backward, each timed with HIP events on the current
@@ -146,7 +239,7 @@ def widened(fa, dev, q, k, v, do, steps=5, warmup=5):
             fn()
             b.record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        return call_stats([a.elapsed_time(b) for a, b in evs])
 
     def case(qq, kk, vv, dd, causal=True, window=None, slopes=None, cfg=""):
         b_, h_, nq, d_ = qq.shape
@@ -155,16 +248,18 @@ def widened(fa, dev, q, k, v, do, steps=5, warmup=5):
         need = fa.bwd_workspace_bytes(b_, h_, nq, d_, H_kv=kk.shape[1], causal=causal, N_k=nk,
                                       window=window)
         ws_ = torch.empty(need, dtype=torch.uint8, device=dev)
-        tf = timed(lambda: fa.fwd(qq, kk, vv, causal=causal, window=window, alibi_slopes=slopes, out=o_, lse=l_))
-        tb = timed(lambda: fa.bwd(qq, kk, vv, o_, dd, l_, causal=causal, workspace=ws_, window=window,
+        sf = timed(lambda: fa.fwd(qq, kk, vv, causal=causal, window=window, alibi_slopes=slopes, out=o_, lse=l_))
+        sb = timed(lambda: fa.bwd(qq, kk, vv, o_, dd, l_, causal=causal, workspace=ws_, window=window,
                                   alibi_slopes=slopes))
+        tf, tb = sf["ms_median"], sb["ms_median"]
         flops = 4.0 * d_ * visible_pairs(nq, nk, causal, window if window is not None else (-1, -1)) * b_ * h_
-        ent = {"config": cfg, "fwd_ms": tf, "bwd_ms": tb,
+        ent = {"config": cfg, "fwd_ms": tf, "bwd_ms": tb, "fwd_calls": sf, "bwd_calls": sb,
                "fwd_tflops": flops / (tf * 1e-3) / 1e12, "bwd_tflops": 2.5 * flops / (tb * 1e-3) / 1e12}
         ent["fwd_frac"] = ent["fwd_tflops"] / PEAK_BF16
         ent["bwd_frac"] = ent["bwd_tflops"] / PEAK_BF16
-        log("widened %-8s fwd %.3f ms %.0f TFLOP/s, bwd %.3f ms %.0f TFLOP/s"
-            % (cfg.split(":")[0], tf, ent["fwd_tflops"], tb, ent["bwd_tflops"]))
+        log("widened %-8s fwd %.3f ms (%.3f..%.3f) %.0f TFLOP/s, bwd %.3f ms (%.3f..%.3f) %.0f TFLOP/s"
+            % (cfg.split(":")[0], tf, sf["ms_min"], sf["ms_max"], ent["fwd_tflops"], tb, sb["ms_min"],
+               sb["ms_max"], ent["bwd_tflops"]))
         return ent
 
     out = {}
@@ -217,7 +312,7 @@ def sweep(fa, dev, steps=10, warmup=5):
             b.record(stream)
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b))
-        return float(np.median(times))
+        return call_stats(times)
 
     g = torch.Generator(device=dev)
     pts = []
@@ -229,19 +324,22 @@ def sweep(fa, dev, steps=10, warmup=5):
             ws = torch.empty(fa.bwd_workspace_bytes(b, 16, n, d), dtype=torch.uint8, device=dev)
             for causal in (True, False):
                 o, lse = fa.fwd(q, k, v, causal=causal)
-                tf = timed(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse))
-                tb = timed(lambda: fa.bwd(q, k, v, o, do, lse, causal=causal, workspace=ws))
+                sf = timed(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse))
+                sb = timed(lambda: fa.bwd(q, k, v, o, do, lse, causal=causal, workspace=ws))
+                tf, tb = sf["ms_median"], sb["ms_median"]
                 fl = fwd_flops(b, 16, n, d, causal)
                 by = fwd_bytes(b, 16, n, d)
                 ent = {"N": n, "B": b, "H": 16, "d": d, "causal": causal,
                        "fwd_ms": tf, "fwd_tflops": fl / (tf * 1e-3) / 1e12, "fwd_gbps": by / (tf * 1e-3) / 1e9,
-                       "bwd_ms": tb, "bwd_tflops": 2.5 * fl / (tb * 1e-3) / 1e12}
+                       "bwd_ms": tb, "bwd_tflops": 2.5 * fl / (tb * 1e-3) / 1e12, "fwd_calls": sf, "bwd_calls": sb}
                 ent["fwd_frac"] = ent["fwd_tflops"] / PEAK_BF16
                 ent["bwd_frac"] = ent["bwd_tflops"] / PEAK_BF16
                 ent["fwd_bound"] = "hbm" if fl / by < ridge else "mfma"
                 if ent["fwd_bound"] == "hbm":
-                    tc = timed(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse), cold=True)
+                    sc_ = timed(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse), cold=True)
+                    tc = sc_["ms_median"]
                     ent["fwd_ms_cold"] = tc
+                    ent["fwd_cold_calls"] = sc_
                     ent["fwd_gbps_cold"] = by / (tc * 1e-3) / 1e9
                     ent["fwd_hbm_frac_cold"] = ent["fwd_gbps_cold"] / PEAK_HBM
                 log("sweep d=%d N=%5d B=%2d causal=%d: fwd %.3f ms %.0f TFLOP/s, bwd %.3f ms %.0f TFLOP/s%s"
@@ -370,7 +468,6 @@ def main():
     ms_step = total_ms / args.steps
 
     breakdown = {}
-    step_flops = 0.0
     dom = None
     for i, (name, _, flops, nbytes, peak) in enumerate(kernels):
         times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
@@ -380,8 +477,9 @@ def main():
             ent["tflops"] = flops / (avg * 1e-3) / 1e12
             ent["pct_of_peak"] = 100.0 * ent["tflops"] / peak
         ent["gbps"] = nbytes / (avg * 1e-3) / 1e9
+        if not flops:
+            ent["pct_of_hbm_peak"] = 100.0 * ent["gbps"] / PEAK_HBM
         breakdown[name] = ent
-        step_flops += flops
         if dom is None or avg > breakdown[dom[0]]["ms_avg"]:
             dom = (name, flops, nbytes, peak)
 
@@ -394,11 +492,32 @@ def main():
         roofline = {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": peak,
                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,
                     "per_launch_flops": flops, "avg_launch_ms": breakdown[name]["ms_avg"],
-                    "algorithmic_bytes": nbytes}
+                    "algorithmic_bytes": nbytes,
+                    "how": "per-launch algorithmic FLOPs / average of the launch's HIP-event times on its "
+                           "stream over the timed steps"}
     else:
         achieved = breakdown[name]["gbps"]
         roofline = {"kernel": name, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM,
                     "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None}
+
+    # The metric: bf16 forward + backward only, from their own times in the steps.
+    value, frac_bf16 = None, None
+    if have_fwd and have_bwd:
+        bf16_ms = breakdown["fa_fwd"]["ms_avg"] + breakdown["fa_bwd"]["ms_avg"]
+        value = 3.5 * fwd_flops(B, H, N, D) / (bf16_ms * 1e-3) / 1e12
+        frac_bf16 = value / PEAK_BF16
+
+    # Shader clock while the bf16 kernels run (outside the timed steps), and the
+    # utilisation against the MFMA peak at that clock (the 2516.6 TFLOP/s spec
+    # assumes 2.4 GHz).
+    sclk = None
+    if args.only is None and have_fwd and have_bwd:
+        sclk = sample_sclk(lambda: (fa.fwd(q, k, v, causal=True, out=o, lse=lse),
+                                    fa.bwd(q, k, v, o, do, lse, causal=True, workspace=ws)))
+        if sclk.get("mhz_median"):
+            sclk["frac_of_peak_at_this_clock"] = frac_bf16 * 2400.0 / sclk["mhz_median"]
+            sclk["roofline_frac_at_this_clock"] = roofline["frac"] * 2400.0 / sclk["mhz_median"]
+        log("sclk: %s" % sclk)
 
     # Context, outside the timed step: the rate of a large bf16 GEMM from the
     # vendor library on this machine, a practical ceiling for dense bf16 MFMA work.
@@ -434,10 +553,13 @@ def main():
         log("timing the CPU oracle on %d heads" % args.cpu_heads)
         cpu = cpu_baseline(args.cpu_heads)
 
-    dtypes = ["bf16"] + (["e4m3"] if have_f8 else [])
     out = {
         "metric": METRIC,
-        "value": step_flops / (ms_step * 1e-3) / 1e12,
+        "value": value,
+        "pct_of_peak": None if frac_bf16 is None else 100.0 * frac_bf16,
+        "value_definition": "bf16 fa_fwd + fa_bwd: 3.5 x 4 B H N^2 d / 2 algorithmic causal FLOPs over the sum "
+                            "of the two calls' average HIP-event times inside the timed steps; the step also "
+                            "runs the fp8 leg (3 x fa_quant_fp8 + fa_fwd_fp8), reported under breakdown",
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -446,7 +568,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "+".join(dtypes),
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "causal attention B=%d H=%d N=%d d=%d (bf16; fp8 leg with 0.1%% x20 "
                                "outliers, Hadamard-rotated Q/K)" % (B, H, N, D),
@@ -454,9 +576,10 @@ def main():
                    "step": [k[0] for k in kernels]},
         "breakdown": breakdown,
         "roofline": roofline,
+        "sclk": sclk,
         "cpu_baseline": cpu,
         "context": {"library_bf16_gemm": gemm},
-        "widened": wid,
+        "widened": wid,  # each row: median of 10 calls, with min / max
         "sweep": swp,
     }
     print(json.dumps(out), flush=True)

@@ -217,11 +217,13 @@ def bwd_workspace_bytes(B, H, N, d, H_kv=None, causal=False, N_k=None, window=No
 
 
 def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, workspace=None, window=None,
-        alibi_slopes=None):
+        alibi_slopes=None, out=None):
     """bf16 backward by recomputation: returns (dQ, dK, dV) bf16.
 
-    Shapes, layouts and masks as in fwd; dK, dV have k's and v's shapes and
-    layouts (for grouped heads, the sums over each group's query heads)."""
+    Shapes, layouts and masks as in fwd; dK, dV have k's and v's shapes (for
+    grouped heads, the sums over each group's query heads). out = (dq, dk, dv)
+    writes into caller-owned views (any layout with a contiguous last
+    dimension); otherwise new tensors take q's, k's and v's layouts."""
     lib = load_library()
     B, H, Hkv, Nq, d = _kv_heads(q, k, v)
     Nk = int(k.shape[2])
@@ -236,7 +238,13 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, w
     need = int(lib.fa_bwd_ext_workspace_bytes(B, H, Hkv, Nq, Nk, d, ctypes.byref(mm)))
     ws = torch.empty(need, dtype=torch.uint8, device=q.device) if workspace is None else workspace
     _check_tensor("workspace", ws, torch.uint8)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        _check_view("dq", dq, (B, H, Nq, d))
+        _check_view("dk", dk, (B, Hkv, Nk, d))
+        _check_view("dv", dv, (B, Hkv, Nk, d))
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
     if m is not None or Nk != Nq:
@@ -268,8 +276,10 @@ def quant_fp8(x, signs=None):
     return x8, sc
 
 
-def fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None):
-    """fp8 forward on quantised inputs: returns (O bf16, LSE fp32)."""
+def fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None,
+            out=None, lse=None):
+    """fp8 forward on quantised inputs: returns (O bf16, LSE fp32); out / lse
+    are optional caller-owned contiguous outputs."""
     lib = load_library()
     B, H, N, d = _bhnd(q8)
     nb = (N + 127) // 128
@@ -277,8 +287,10 @@ def fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: 
         _check_tensor(n, t, torch.uint8, (B, H, N, d))
     for n, t in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
         _check_tensor(n, t, torch.float32, (B, H, nb))
-    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
+    _check_tensor("out", o, torch.bfloat16, (B, H, N, d))
+    _check_tensor("lse", lse, torch.float32, (B, H, N))
     st = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
                         k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), lse.data_ptr(),
                         B, H, N, d, int(bool(causal)), _scale(scale, d), _stream())

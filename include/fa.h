@@ -28,6 +28,11 @@
  * - Arguments are validated before anything is launched. On error nothing is
  *   written and a status below is returned; the library never prints or aborts.
  * - Forward calls are bitwise deterministic for fixed inputs and shape.
+ * - Inputs are finite: NaN or infinite values in q, k, v, o, dO, lse (except
+ *   the -inf LSE of a query that sees no key) or the fp8 scales are outside the
+ *   contract. The kernels are built assuming no NaN operands (maxima compile to
+ *   plain v_max), so such inputs give unspecified outputs, not an error status
+ *   and not necessarily NaN.
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H

@@ -312,11 +312,6 @@ def general_head_cols(q, k, v, do, cols, causal: bool, scale: float, window=(-1,
     return dk, dv
 
 
-def row_delta(o, do):
-    """D_i = sum_k dO_ik O_ik (equal to sum_j P_ij dP_ij because O = P V)."""
-    return (_f64(o) * _f64(do)).sum(axis=-1)
-
-
 def backward_head_rows(q, k, v, do, rows, causal: bool, scale: float):
     """dQ for the selected query rows of one head.
 

@@ -63,22 +63,19 @@ def test_bwd_n4096_d128_causal(gpu):
     _check_grads(got, ref, "bwd n4096")
 
 
-def test_bwd_n8192_d128_causal_sampled(gpu):
-    """N = 8192 (the headline backward shape): sampled dQ rows and dK/dV rows of two heads."""
+def test_bwd_n8192_d128_causal_whole(gpu):
+    """N = 8192 (the headline backward shape: the forward workload's Q, K, V
+    plus dO from the same seed): every element of dQ, dK, dV of all 32 heads
+    against the fp64 oracle (whole-tensor rel-RMS), the worst head reported."""
     B, H, N, d = 2, 16, 8192, 128
     host, dev, _, got = _run(gpu, B, H, N, d, True, 3)
-    dq, dk, dv = (to_host(t) for t in got)
-    for t in (dq, dk, dv):
-        assert np.isfinite(t).all()
-    idx = np.unique(np.concatenate([[0, 1, 127, 128, 4095, 8190, 8191],
-                                    np.random.default_rng(1).integers(0, N, 16)]))
-    scale = 1.0 / math.sqrt(d)
-    for b, h in ((0, 0), (1, 9)):
-        args = (host["q"][b, h], host["k"][b, h], host["v"][b, h], host["do"][b, h])
-        rq = A.backward_head_rows(*args, idx, True, scale)
-        rk, rv = A.backward_head_cols(*args, idx, True, scale)
-        _check_grads([dq[b, h, idx], dk[b, h, idx], dv[b, h, idx]], [rq, rk, rv],
-                     "n8192 head (%d,%d)" % (b, h))
+    got = [to_host(t) for t in got]
+    del dev
+    ref = A.backward(host["q"], host["k"], host["v"], host["do"], True, 1.0 / math.sqrt(d))
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        worst = max(((A.rel_rms(g[b, h], r[b, h]), b, h) for b in range(B) for h in range(H)))
+        print("n8192 %s worst head (%d,%d) rel_rms=%.3e" % (name, worst[1], worst[2], worst[0]), flush=True)
+    _check_grads(got, ref, "bwd n8192 whole tensor")
 
 
 def test_bwd_deterministic(gpu):

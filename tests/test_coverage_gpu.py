@@ -1,0 +1,108 @@
+"""Output coverage: every output element written exactly inside its tensor.
+
+Each output is carved out of a larger device buffer (tests/gpu_util.Guarded):
+the output itself is NaN-filled before the call, and sentinel regions sit
+directly before and after it. After the call every output element must be
+finite (a tile, row or column a kernel skipped would stay NaN, whatever the
+caching allocator held before) and every sentinel bit unchanged (no write past
+either end). The values are also compared with the fp64 oracle.
+
+Backward cases cover each write path of the gradients: the plain key-stationary
+epilogue, grouped heads whose key blocks are split over workgroups (fp32
+partials summed by a reduction kernel), d = 256 (two workgroups per key block,
+one per half of the dK / dV columns), and key blocks that no query sees (dK,
+dV written as zeros). The fp8 forward's O and LSE are guarded the same way.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs
+from oracle import attention as A
+from oracle import fp8 as F
+from gpu_util import FP8_O_REL_RMS, GRAD_REL_RMS, Guarded, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _grads_guarded(gpu, B, H, Hkv, Nq, Nk, d, causal, window, seed):
+    tag = "B%d H%d Hkv%d Nq%d Nk%d d%d c%d w%s" % (B, H, Hkv, Nq, Nk, d, causal, window)
+    print(tag, flush=True)
+    a = fa_inputs.grouped_inputs(B, H, Hkv, Nq, d, seed, with_do=True)
+    b = fa_inputs.grouped_inputs(B, H, Hkv, Nk, d, seed + 1)
+    x = {"q": a["q"], "do": a["do"], "k": b["k"], "v": b["v"]}
+    dev = {n: to_dev(x[n]) for n in x}
+    o, lse = gpu.fwd(dev["q"], dev["k"], dev["v"], causal=causal, window=window)
+    gq = Guarded((B, H, Nq, d), torch.bfloat16)
+    gk = Guarded((B, Hkv, Nk, d), torch.bfloat16)
+    gv = Guarded((B, Hkv, Nk, d), torch.bfloat16)
+    gpu.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=causal, window=window,
+            out=(gq.t, gk.t, gv.t))
+    torch.cuda.synchronize()
+    for name, g in (("dQ", gq), ("dK", gk), ("dV", gv)):
+        g.check("%s %s" % (tag, name))
+    ref = A.backward_general(x["q"], x["k"], x["v"], x["do"], causal, 1.0 / math.sqrt(d),
+                             window if window is not None else (-1, -1))
+    for name, g, r in zip(("dQ", "dK", "dV"), (gq.t, gk.t, gv.t), ref):
+        got = to_host(g)
+        if np.linalg.norm(r) == 0.0:
+            assert np.abs(got).max() <= 1e-4, (tag, name)
+            continue
+        e = A.rel_rms(got, r)
+        print("%s %s rel_rms=%.3e" % (tag, name, e), flush=True)
+        assert e <= GRAD_REL_RMS, (tag, name, e)
+    return ref
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_outputs_covered_plain(gpu, d, causal):
+    """Contiguous multi-head backward (fa_bwd), ragged N over several key blocks."""
+    _grads_guarded(gpu, 2, 3, 3, 777, 777, d, causal, None, 7100 + d)
+
+
+def test_bwd_outputs_covered_grouped_split(gpu):
+    """H = 8 on H_kv = 2, short N: each key block's four query heads are split
+    over workgroups that leave fp32 partials for the reduction kernel."""
+    B, H, Hkv, N, d = 1, 8, 2, 300, 64
+    ws = gpu.bwd_workspace_bytes(B, H, N, d, H_kv=Hkv, causal=True)
+    assert ws > gpu.bwd_workspace_bytes(B, H, N, d), "expected the split (partials) path"
+    _grads_guarded(gpu, B, H, Hkv, N, N, d, True, None, 7200)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_outputs_covered_d256(gpu, causal):
+    """d = 256: two workgroups per key block, each writing one half of the dK / dV columns."""
+    _grads_guarded(gpu, 1, 2, 2, 300, 300, 256, causal, None, 7300)
+
+
+def test_bwd_outputs_covered_unseen_key_blocks(gpu):
+    """64 queries on 1024 keys, causal, 32-key window: query i sees keys
+    928 + i .. 960 + i only, so key blocks 0 .. 6 are seen by no query and the
+    dK / dV rows there must be written as zeros."""
+    ref = _grads_guarded(gpu, 1, 2, 2, 64, 1024, 128, True, (32, 0), 7400)
+    assert np.all(ref[1][:, :, :896] == 0.0) and np.all(ref[2][:, :, :896] == 0.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_fp8_outputs_covered(gpu, d, causal):
+    B, H, N = 2, 3, 777
+    host = fa_inputs.attention_inputs(B, H, N, d, 7500 + d, outliers=True)
+    dev = {n: to_dev(host[n]) for n in host}
+    qz = {n: gpu.quant_fp8(dev[n]) for n in ("q", "k", "v")}
+    go = Guarded((B, H, N, d), torch.bfloat16)
+    gl = Guarded((B, H, N), torch.float32)
+    gpu.fwd_fp8(qz["q"][0], qz["k"][0], qz["v"][0], qz["q"][1], qz["k"][1], qz["v"][1], causal=causal,
+                out=go.t, lse=gl.t)
+    torch.cuda.synchronize()
+    go.check("fp8 O d%d c%d" % (d, causal))
+    gl.check("fp8 LSE d%d c%d" % (d, causal))
+    deq = {n: F.dequantize(qz[n][0].cpu().numpy(), qz[n][1].cpu().numpy()) for n in ("q", "k", "v")}
+    r_o, _ = A.forward(deq["q"], deq["k"], deq["v"], causal, 1.0 / math.sqrt(d))
+    e = A.rel_rms(to_host(go.t), r_o)
+    print("fp8 guarded d%d c%d rel_rms=%.3e" % (d, causal, e), flush=True)
+    assert e <= FP8_O_REL_RMS

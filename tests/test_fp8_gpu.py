@@ -22,11 +22,18 @@ from gpu_util import FP8_O_REL_RMS, inputs_on_device, to_host
 
 pytestmark = pytest.mark.gpu
 
-# The e4m3 MFMA (v_mfma_f32_32x32x64_f8f6f4) does not accumulate exactly: on
-# full-range random e4m3 operands its 64-term dot products were measured off
-# by up to 1.6e-4 of sum |a_k b_k|. LSE is 1-Lipschitz in the scores, so
+# The e4m3 MFMA (v_mfma_f32_32x32x64_f8f6f4) does not accumulate exactly. Its
+# products are summed on a grid of about 2^-16 of the largest product of the
+# instruction's 64, so each smaller product can lose up to half a grid step:
+# |dS| <= 32 * 2^-16 * max_k |a_k b_k| <= 4.9e-4 * sum_k |a_k b_k| per
+# instruction. The worst case is one large product among small ones (a query
+# outlier meeting a key outlier at the same coordinate, as in the fp8
+# workload without rotation): measured up to 4.4e-4 of sum |a_k b_k|
+# (test_fp8_mfma_accumulation_error measures it through fa_fwd_fp8). MFMA_REL
+# leaves a factor of two over that model, which also covers the second
+# instruction at d = 128. LSE is 1-Lipschitz in the scores, so
 # |dLSE_i| <= MFMA_REL * scale * max_j sum_d |q_id k_jd| (dequantised values).
-MFMA_REL = 3e-4
+MFMA_REL = 1e-3
 
 
 def lse_bound(q, k, scale, causal, rows=None):
@@ -136,26 +143,89 @@ def test_fwd_fp8_workgroup_shape_boundary(gpu, N):
 
 
 @pytest.mark.parametrize("rot", [False, True])
-def test_fwd_fp8_n8192_sampled(gpu, rot):
-    """The fp8 workload: B=2, H=16, N=8192, d=128, causal, 0.1% x20 outliers;
-    sampled rows of three heads, both readings."""
+def test_fwd_fp8_n8192_whole(gpu, rot):
+    """The fp8 workload: B=2, H=16, N=8192, d=128, causal, 0.1% x20 outliers,
+    rotation off and on; every element of all 32 heads. Reading (i) is gated
+    (whole-tensor rel-RMS of O, every LSE within the MFMA accumulation bound);
+    reading (ii) is printed."""
     B, H, N, d = 2, 16, 8192, 128
     host, deq, o, lse = _fp8_case(gpu, B, H, N, d, True, rot, 5)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 8191],
-                                     np.random.default_rng(2).integers(0, N, 40)]))
     scale = 1.0 / math.sqrt(d)
-    errs, e2es = [], []
-    for b, h in ((0, 0), (1, 5), (0, 11)):
-        r_o, r_l = A.forward_head(deq["q"][b, h], deq["k"][b, h], deq["v"][b, h], True, scale, rows)
-        x_o, _ = A.forward_head(host["q"][b, h], host["k"][b, h], host["v"][b, h], True, scale, rows)
-        errs.append(A.rel_rms(o[b, h, rows], r_o))
-        e2es.append(A.rel_rms(o[b, h, rows], x_o))
-        bnd = lse_bound(deq["q"][b, h], deq["k"][b, h], scale, True, rows)
-        assert np.all(np.abs(lse[b, h, rows] - r_l) <= bnd)
-    print("fp8 n8192 rot%d: (i) rel_rms per head %s  (ii) end-to-end %s"
-          % (rot, ["%.3e" % x for x in errs], ["%.3e" % x for x in e2es]), flush=True)
-    assert max(errs) <= FP8_O_REL_RMS
+    r_o, r_l = A.forward(deq["q"], deq["k"], deq["v"], True, scale)
+    e = A.rel_rms(o, r_o)
+    worst = max(((A.rel_rms(o[b, h], r_o[b, h]), b, h) for b in range(B) for h in range(H)))
+    ratio = 0.0
+    for b in range(B):
+        for h in range(H):
+            bnd = lse_bound(deq["q"][b, h], deq["k"][b, h], scale, True)
+            ratio = max(ratio, float(np.max(np.abs(lse[b, h] - r_l[b, h]) / bnd)))
+    del r_o, r_l
+    x_o, x_l = A.forward(host["q"], host["k"], host["v"], True, scale)
+    e2e = A.rel_rms(o, x_o)
+    print("fp8 n8192 rot%d: (i) rel_rms=%.3e (worst head (%d,%d) %.3e), max |dLSE|/bound=%.3f; "
+          "(ii) end-to-end rel_rms=%.3e, LSE abs=%.3e"
+          % (rot, e, worst[1], worst[2], worst[0], ratio, e2e, A.max_abs(lse, x_l)), flush=True)
+    assert e <= FP8_O_REL_RMS
+    assert ratio <= 1.0, "LSE outside the MFMA accumulation bound"
+
+
+def _codes_uniform(rng, shape):
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    return rng.choice(finite, size=shape)
+
+
+def _codes_normal(rng, shape):
+    """A 128-row block without outliers: values N(0, 1) * 448 / 4.5."""
+    return F.e4m3_encode((rng.standard_normal(shape) * (448.0 / 4.5)).astype(np.float32))
+
+
+def _codes_one_large(rng, shape, cols):
+    """The pattern of an outlier block meeting an outlier at the same
+    coordinate: values N(0, 1) * 448 / 60 (the block's scale set by an
+    outlier of another row), and one coordinate per row of magnitude 200 .. 260
+    (its product with the other operand's is near 2^16)."""
+    x = rng.standard_normal(shape) * (448.0 / 60.0)
+    rows = np.arange(shape[1])
+    x[0, rows, 0, cols] = rng.uniform(200.0, 260.0, size=shape[1]) * rng.choice([-1.0, 1.0], size=shape[1])
+    return F.e4m3_encode(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("dist", ["uniform", "normal", "one_large"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_mfma_accumulation_error(gpu, d, dist):
+    """The accumulation error of the e4m3 score products, measured through
+    fa_fwd_fp8 itself: with one key (N = 1) the LSE is exactly scale * q . k of
+    the decoded codes (all block scales 1). Three code distributions: uniform
+    over every finite e4m3 value (full range), a normal block, and one large
+    product among small ones (the worst case of the accumulation grid). The
+    largest ratio |error| / (scale sum_d |q_d k_d|) over 1024 dot products is
+    checked against MFMA_REL."""
+    B, H, N = 1, 1024, 1
+    rng = np.random.default_rng(1234 + d)
+    if dist == "uniform":
+        codes = {n: _codes_uniform(rng, (B, H, N, d)) for n in ("q", "k", "v")}
+    elif dist == "normal":
+        codes = {n: _codes_normal(rng, (B, H, N, d)) for n in ("q", "k", "v")}
+    else:
+        cols = rng.integers(0, d, size=H)
+        codes = {n: _codes_one_large(rng, (B, H, N, d), cols) for n in ("q", "k", "v")}
+    dev = {n: torch.from_numpy(codes[n]).cuda() for n in codes}
+    ones = torch.ones((B, H, 1), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(d)
+    o, lse = gpu.fwd_fp8(dev["q"], dev["k"], dev["v"], ones, ones, ones, causal=True)
+    torch.cuda.synchronize()
+    qv = F.e4m3_decode(codes["q"]).astype(np.float64)[:, :, 0]
+    kv = F.e4m3_decode(codes["k"]).astype(np.float64)[:, :, 0]
+    s32 = float(np.float32(scale))  # the scale as the kernel receives it
+    exact = s32 * (qv * kv).sum(-1)
+    mag = s32 * np.abs(qv * kv).sum(-1)
+    got = lse.cpu().numpy().astype(np.float64)[:, :, 0]
+    rel = np.abs(got - exact) / mag
+    print("fp8 MFMA d%d %s: max |err| / (scale sum |q k|) = %.3e (median %.3e) over %d products"
+          % (d, dist, rel.max(), np.median(rel), rel.size), flush=True)
+    assert np.isfinite(got).all()
+    assert rel.max() <= MFMA_REL
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -60,24 +60,22 @@ def test_fwd_several_tiles_d(gpu, d):
     _full(gpu, 2, 3, 1000, d, True, 77)
 
 
-def test_fwd_n8192_d128_causal_sampled(gpu):
-    """Full-size workload (2 x 16 x 8192 x 128, causal): sampled rows vs the oracle,
-    plus properties of every output."""
+def test_fwd_n8192_d128_causal_whole(gpu):
+    """Full-size workload (2 x 16 x 8192 x 128, causal): every element of O and
+    LSE of all 32 heads against the fp64 oracle (whole-tensor max-abs and
+    rel-RMS), the worst head reported."""
     B, H, N, d = 2, 16, 8192, 128
     host, dev = inputs_on_device(B, H, N, d, 3)
     o, lse = gpu.fwd(dev["q"], dev["k"], dev["v"], causal=True)
     torch.cuda.synchronize()
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 255, 256, 4095, 4096, 8191],
-                                     np.random.default_rng(0).integers(0, N, 40)]))
-    o_h = to_host(o)
-    lse_h = to_host(lse)
-    for b, h in ((0, 0), (1, 15), (0, 7)):
-        o_ref, lse_ref = A.forward_head(host["q"][b, h], host["k"][b, h], host["v"][b, h], True,
-                                        1.0 / math.sqrt(d), rows)
-        _check(o_h[b, h, rows], lse_h[b, h, rows], o_ref, lse_ref, "n8192 head (%d,%d)" % (b, h))
     # causal row 0 sees only key 0: O_0 = V_0 exactly
     assert torch.equal(o[:, :, 0], dev["v"][:, :, 0])
+    o_h, lse_h = to_host(o), to_host(lse)
+    del o, lse, dev
+    o_ref, lse_ref = A.forward(host["q"], host["k"], host["v"], True, 1.0 / math.sqrt(d))
+    worst = max(((A.rel_rms(o_h[b, h], o_ref[b, h]), b, h) for b in range(B) for h in range(H)))
+    print("n8192 worst head (%d,%d) rel_rms=%.3e" % (worst[1], worst[2], worst[0]), flush=True)
+    _check(o_h, lse_h, o_ref, lse_ref, "n8192 whole tensor")
 
 
 def test_fwd_deterministic_and_covers_outputs(gpu):

@@ -350,3 +350,18 @@ def test_planted_mistakes_are_caught(monkeypatch, target, replacement, pins):
     for name in pins:
         with pytest.raises((AssertionError, ValueError, FloatingPointError)):
             runners[name]()
+
+
+def test_default_scale_is_inverse_sqrt_d():
+    """[HUB] "How it works": scores are divided by sqrt(d). Exact values at
+    d = 4, 64 and 256, and a forward without a scale equals one with 1/sqrt(d)
+    for a hand-checkable case (d = 4, two keys, causal row 1)."""
+    assert A.default_scale(4) == 0.5 and A.default_scale(64) == 0.125 and A.default_scale(256) == 0.0625
+    q = np.array([[[[2.0, 0.0, 0.0, 0.0], [2.0, 0.0, 0.0, 0.0]]]])
+    k = np.array([[[[1.0, 0.0, 0.0, 0.0], [0.0, 0.0, 0.0, 0.0]]]])
+    v = np.array([[[[1.0, 0.0, 0.0, 0.0], [0.0, 1.0, 0.0, 0.0]]]])
+    o, lse = A.forward(q, k, v, True)
+    # row 1: scores s * (2, 0) = (1, 0) with s = 1/2, so P = (e, 1) / (e + 1)
+    e = math.e
+    assert np.allclose(o[0, 0, 1], [e / (e + 1), 1 / (e + 1), 0, 0], rtol=0, atol=1e-15)
+    assert abs(lse[0, 0, 1] - math.log(e + 1)) < 1e-15

@@ -29,6 +29,7 @@ LIB_PATH = os.path.join(_HERE, "libfa_mi355x.so")
 FA_STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_ALIGN",
     5: "FA_ERR_WORKSPACE", 6: "FA_ERR_DEVICE", 7: "FA_ERR_ALIAS", 8: "FA_ERR_LAUNCH", 9: "FA_ERR_ARG",
+    10: "FA_ERR_SCRATCH",
 }
 
 _lib = None
@@ -55,6 +56,7 @@ SIGNATURES = {
     "fa_fwd_strided": (_I, [_P] * 5 + [_I, _I, _I, _I, _I, _P, _I, _F, _P]),
     "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "fa_bwd": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _F, _P, ctypes.c_size_t, _P]),
+    "fa_bwd_noalloc": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _F, _P]),
     "fa_bwd_strided": (_I, [_P] * 9 + [_I, _I, _I, _I, _I, _P, _I, _F, _P, ctypes.c_size_t, _P]),
     "fa_bwd_strided_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),
     "fa_fwd_ext": (_I, [_P] * 5 + [_I] * 6 + [_P, _P, _F, _P]),
@@ -258,6 +260,28 @@ def bwd(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, w
         st = lib.fa_bwd_strided(*ptrs, B, H, Hkv, Nq, d, _strides(q, k, v, o, do, dq, dk, dv), c, sc,
                                 ws.data_ptr(), ws.numel(), _stream())
         _raise(st, "fa_bwd_strided")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None, out=None):
+    """fa_bwd_noalloc: the contiguous multi-head backward with no workspace
+    argument (the library's static per-GPU scratch holds D). Calls that overlap
+    on one GPU race on that scratch. out = (dq, dk, dv) contiguous, else new."""
+    lib = load_library()
+    B, H, N, d = _bhnd(q)
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_tensor(n, t, torch.bfloat16, (B, H, N, d))
+    _check_tensor("lse", lse, torch.float32, (B, H, N))
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        for n, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            _check_tensor(n, t, torch.bfloat16, (B, H, N, d))
+    st = lib.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, int(bool(causal)),
+                            _scale(scale, d), _stream())
+    _raise(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <utility>
 
 #include "../../include/fa.h"
@@ -143,6 +144,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps another tensor";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
     case FA_ERR_ARG: return "FA_ERR_ARG: bad causal flag, window, scale or stride";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: B*H*N exceeds the static scratch of fa_bwd_noalloc";
     default: return "FA_ERR_UNKNOWN";
   }
 }
@@ -208,10 +210,43 @@ size_t fa_bwd_strided_workspace_bytes(int B, int H, int H_kv, int N, int d, int 
   return fa_bwd_ext_workspace_bytes(B, H, H_kv, N, N, d, &m);
 }
 
-int fa_bwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
-               const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
-               int B, int H, int H_kv, int N_q, int N_k, int d, const fa_strides* st, const fa_mask* mask,
-               float scale, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Static scratch of fa_bwd_noalloc: the fp32 row vector D (the only
+// workspace fa_bwd needs when H_kv = H). Each GPU the library runs on holds
+// its own copy until the process ends. In host code `scratch` only names the
+// symbol; its device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = FA_BWD_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch (the current device), or NULL.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) return nullptr;
+    p = a;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+// The backward of fa_bwd_ext. With noalloc the workspace comes from the
+// static scratch instead of (ws, ws_bytes), which are then ignored.
+int bwd_impl(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o, const uint16_t* dO,
+             const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv, int B, int H, int H_kv, int N_q, int N_k,
+             int d, const fa_strides* st, const fa_mask* mask, float scale, void* ws, size_t ws_bytes,
+             void* stream, bool noalloc) {
   if (!scale_ok(scale) || !mask_ok(mask)) return FA_ERR_ARG;
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv || !st) return FA_ERR_NULL;
   if (!bf16_head_dim(d)) return FA_ERR_HEADDIM;
@@ -227,19 +262,39 @@ int fa_bwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v, const ui
   const float* slopes = mask ? mask->alibi_slopes : nullptr;
   if (!aligned16(lse) || ((uintptr_t)slopes & 3u)) return FA_ERR_ALIGN;
   const size_t need = fa_bwd_ext_workspace_bytes(B, H, H_kv, N_q, N_k, d, mask);
-  if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need) return FA_ERR_WORKSPACE;
+  if (noalloc) {
+    if (need > kNoAllocScratchBytes) return FA_ERR_SCRATCH;
+  } else if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < need) {
+    return FA_ERR_WORKSPACE;
+  }
   const size_t lb = (size_t)B * H * N_q * 4;
   const Range ins[7] = {vq.range(), vk.range(), vv.range(), vo.range(), vdo.range(), span(lse, lb),
                         span(slopes, slopes ? (size_t)H * 4 : 0)};
-  const Range outs[4] = {vdq.range(), vdk.range(), vdv.range(), span(ws, need)};
+  const Range outs[4] = {vdq.range(), vdk.range(), vdv.range(), span(noalloc ? nullptr : ws, noalloc ? 0 : need)};
   if (!vdq.injective() || !vdk.injective() || !vdv.injective() || any_alias(outs, 4, ins, 7)) return FA_ERR_ALIAS;
   if (int s = check_device()) return s;
+  if (noalloc) {
+    ws = scratch_ptr();
+    if (!ws) return FA_ERR_DEVICE;
+  }
   auto S = [&](int i) { return fa::Strides{st[i].batch, st[i].head, st[i].row}; };
   fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, (float*)ws, B, H, H_kv, N_q, N_k, d,
                 band_of(mask, N_q, N_k), slopes, scale, S(0), S(1), S(2), S(3), S(4), S(5), S(6), S(7), stream};
   a.split = fa::bwd_kv_split(B, H_kv, H / H_kv, N_k, uneven(mask));
   a.part = a.split > 1 ? (float*)((char*)ws + fa::bwd_delta_bytes(B, H, N_q)) : nullptr;
   return fa::launch_bwd(a) ? FA_ERR_LAUNCH : FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+               const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+               int B, int H, int H_kv, int N_q, int N_k, int d, const fa_strides* st, const fa_mask* mask,
+               float scale, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, H_kv, N_q, N_k, d, st, mask, scale, ws, ws_bytes, stream,
+                  false);
 }
 
 int fa_bwd_strided(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
@@ -258,6 +313,16 @@ int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16
   const fa_strides c{(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
   const fa_strides st[8] = {c, c, c, c, c, c, c, c};
   return fa_bwd_strided(q, k, v, o, dO, lse, dq, dk, dv, B, H, H, N, d, st, causal, scale, ws, ws_bytes, stream);
+}
+
+int fa_bwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                   const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                   int B, int H, int N, int d, int causal, float scale, void* stream) {
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  const fa_strides c{(int64_t)H * N * d, (int64_t)N * d, (int64_t)d};
+  const fa_strides st[8] = {c, c, c, c, c, c, c, c};
+  const fa_mask m{causal, -1, -1, nullptr};
+  return bwd_impl(q, k, v, o, dO, lse, dq, dk, dv, B, H, H, N, N, d, st, &m, scale, nullptr, 0, stream, true);
 }
 
 int fa_quant_fp8(const uint16_t* x, uint8_t* x8, float* scales, const int8_t* signs_or_null,

@@ -17,8 +17,9 @@
  *   head dim) order of PyTorch's scaled_dot_product_attention. Per-row vectors
  *   (LSE) are [B, H, N] float32. bf16 values travel as their uint16_t bits.
  * - Every tensor pointer is a DEVICE pointer owned by the caller, 16-byte
- *   aligned, on the current HIP device. The library never allocates, frees or
- *   keeps device memory; the backward workspace comes from the caller.
+ *   aligned, on the current HIP device. The library never allocates or frees
+ *   device memory; the backward workspace comes from the caller. The only
+ *   device memory it holds is the static scratch array of fa_bwd_noalloc.
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream). All
  *   calls are asynchronous on that stream; a device fault surfaces at the
  *   caller's next synchronisation.
@@ -44,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 enum fa_status {
   FA_OK = 0,
@@ -56,8 +57,9 @@ enum fa_status {
   FA_ERR_DEVICE = 6,    /* no HIP device, or the current device is not gfx950 */
   FA_ERR_ALIAS = 7,     /* an output overlaps an input, another output or itself */
   FA_ERR_LAUNCH = 8,    /* the kernel launch failed (hipGetLastError) */
-  FA_ERR_ARG = 9        /* causal not 0/1, a window side < -1 or > 2^24, scale not finite and positive,
+  FA_ERR_ARG = 9,       /* causal not 0/1, a window side < -1 or > 2^24, scale not finite and positive,
                            a stride < 1, or a row stride >= 2^31 */
+  FA_ERR_SCRATCH = 10   /* fa_bwd_noalloc: 4 * B * H * N bytes exceed FA_BWD_NOALLOC_SCRATCH_BYTES */
 };
 
 /*
@@ -142,6 +144,28 @@ int fa_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16
            const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
            int B, int H, int N, int d, int causal, float scale, void* ws, size_t ws_bytes,
            void* stream);
+
+/*
+ * fa_bwd without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory at the point of the call: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * library calls no hipMalloc, hipFree or allocating routine here; the fp32
+ * D = rowsum(dO o O) vector that fa_bwd keeps in the caller's workspace lives
+ * instead in a static device array of FA_BWD_NOALLOC_SCRATCH_BYTES (8 MiB, so
+ * B * H * N <= 2^21 rows), one per GPU, held until the process ends.
+ * Arguments, layouts, results and determinism are those of fa_bwd; the
+ * results are bitwise identical to fa_bwd's (the same kernels run).
+ *   returns FA_ERR_SCRATCH when 4 * B * H * N > FA_BWD_NOALLOC_SCRATCH_BYTES,
+ *   checked on the host before anything is launched.
+ * Every call on one GPU shares that GPU's array and leaves its D there (the
+ * next call overwrites all of it before reading it; nothing needs clearing).
+ * Calls that overlap in time on one GPU (two streams, or two host threads)
+ * race on the array and give wrong gradients: serialise them.
+ */
+#define FA_BWD_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int fa_bwd_noalloc(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* o,
+                   const uint16_t* dO, const float* lse, uint16_t* dq, uint16_t* dk, uint16_t* dv,
+                   int B, int H, int N, int d, int causal, float scale, void* stream);
 
 /*
  * fa_bwd on strided views with grouped key/value heads (see fa_fwd_strided):

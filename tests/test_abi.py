@@ -36,9 +36,9 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_version_and_status_strings():
-    assert fa.abi_version() == 3
+    assert fa.abi_version() == 4
     codes = declared_status_codes()
-    assert codes["FA_OK"] == 0 and len(codes) == 10
+    assert codes["FA_OK"] == 0 and len(codes) == 11
     for name, val in codes.items():
         assert fa.FA_STATUS[val] == name
         assert fa.status_string(val).startswith(name)
@@ -246,3 +246,41 @@ def test_ext_no_device_is_reported_after_validation():
     st8 = _st(cq, ck, ck, cq, cq, cq, ck, ck)
     need = lib.fa_bwd_ext_workspace_bytes(B, H, Hkv, Nq, Nk, d, None)
     assert lib.fa_bwd_ext(*ptrs, B, H, Hkv, Nq, Nk, d, st8, None, 0.1, 0x40000000, need, None) == 6
+
+
+def test_bwd_noalloc_rejects_bad_arguments():
+    """fa_bwd_noalloc: host validation as fa_bwd (no workspace argument), and
+    FA_ERR_SCRATCH, before any HIP call, when D would not fit the static
+    scratch (4 bytes per row, FA_BWD_NOALLOC_SCRATCH_BYTES = 8 MiB)."""
+    lib = fa.load_library()
+    good = [P + i * 0x100000 for i in range(9)]
+    args = good + [1, 1, 64, 64, 1, 0.125, None]
+    bad = list(args)
+    bad[6] = good[0]                    # dq aliases q
+    assert lib.fa_bwd_noalloc(*bad) == 7
+    bad = list(args)
+    bad[5] = None                       # NULL lse
+    assert lib.fa_bwd_noalloc(*bad) == 1
+    bad = list(args)
+    bad[12] = 96                        # head dim
+    assert lib.fa_bwd_noalloc(*bad) == 3
+    bad = list(args)
+    bad[13] = 2                         # causal flag
+    assert lib.fa_bwd_noalloc(*bad) == 9
+    # 2^21 + 64 rows of D (each tensor 1 GiB + 16 KiB apart): one row block too many
+    rows_max = (8 << 20) // 4
+    B, H, N, d = 1, 1, rows_max + 64, 64
+    span = 2 * N * d
+    big = [P + i * (span + 0x100000) for i in range(9)]
+    assert lib.fa_bwd_noalloc(*big, B, H, N, d, 0, 0.125, None) == 10
+    assert fa.status_string(10).startswith("FA_ERR_SCRATCH")
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="valid-looking fake pointers must never reach a GPU")
+def test_bwd_noalloc_no_device_is_reported_after_validation():
+    lib = fa.load_library()
+    rows_max = (8 << 20) // 4
+    N, d = rows_max, 64               # exactly fills the scratch
+    span = 2 * N * d
+    ptrs = [P + i * (span + 0x100000) for i in range(9)]
+    assert lib.fa_bwd_noalloc(*ptrs, 1, 1, N, d, 1, 0.125, None) == 6

@@ -502,7 +502,7 @@ def main():
 
     # The metric: bf16 forward + backward only, from their own times in the steps.
     value, frac_bf16 = None, None
-    if have_fwd and have_bwd:
+    if "fa_fwd" in breakdown and "fa_bwd" in breakdown:
         bf16_ms = breakdown["fa_fwd"]["ms_avg"] + breakdown["fa_bwd"]["ms_avg"]
         value = 3.5 * fwd_flops(B, H, N, D) / (bf16_ms * 1e-3) / 1e12
         frac_bf16 = value / PEAK_BF16
@@ -511,7 +511,7 @@ def main():
     # utilisation against the MFMA peak at that clock (the 2516.6 TFLOP/s spec
     # assumes 2.4 GHz).
     sclk = None
-    if args.only is None and have_fwd and have_bwd:
+    if args.only is None and value is not None:
         sclk = sample_sclk(lambda: (fa.fwd(q, k, v, causal=True, out=o, lse=lse),
                                     fa.bwd(q, k, v, o, do, lse, causal=True, workspace=ws)))
         if sclk.get("mhz_median"):

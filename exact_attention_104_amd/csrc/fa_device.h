@@ -70,7 +70,11 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // behind a wait for these loads (it cannot tell the buffers apart once the
 // buffer is chosen at run time). Every caller waits explicitly with
 // wait_vmem_all() and a barrier before reading what they wrote. M0 (the LDS
-// base operand) is saved and restored around the load.
+// base operand) is saved and restored around the load: M0 is a reserved
+// register, which a clobber list cannot name (the compiler warns that such a
+// clobber is not honoured), and the "s" / "=&s" operands come from the
+// allocatable SGPRs, which exclude M0. The kernels here never use M0
+// otherwise (checked in the generated code).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

@@ -184,9 +184,11 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     // At d = 256 the lane index passes through an empty asm so that the LDS
     // addresses derived from it are formed here rather than hoisted out of the
     // tile loop (64 of them would not fit in registers). Not in the ALiBi
-    // instance: there this variant gave wrong results for windowed ALiBi
-    // (the asm is semantically empty; without it the results are right, at
-    // the cost of a few spilled registers).
+    // instance: built that way, its element mask came out wrong on band-edge
+    // tiles handled by the second of the two unrolled copies of this body,
+    // only with a window and ALiBi together (the source is equivalent; the
+    // generated code is at fault). Without the asm it is right, at the cost
+    // of a few spilled registers.
     constexpr bool PIN = D == 256 && !ALIBI;
     int lp = lane;
     if constexpr (PIN) asm volatile("" : "+v"(lp));

@@ -24,7 +24,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfa_mi355x.so")
+# FA_MI355X_LIB names another build of the same library (e.g. the
+# host-sanitized one, for CPU tests of the C ABI).
+LIB_PATH = os.environ.get("FA_MI355X_LIB") or os.path.join(_HERE, "libfa_mi355x.so")
 
 FA_STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEADDIM", 4: "FA_ERR_ALIGN",

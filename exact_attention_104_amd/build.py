@@ -3,6 +3,13 @@
 Each ``csrc/*.hip`` file is compiled by hipcc for gfx950 only, then linked into
 one shared library that exports the C ABI of ``include/fa.h``. Run
 ``python -m exact_attention_104_amd.build`` (or ``__graft_entry__.build()``).
+
+``build(sanitize=True)`` (``python -m exact_attention_104_amd.build --host-sanitize``)
+builds ``libfa_mi355x_hostsan.so`` instead: the same sources with the host
+code (argument validation, dispatch) instrumented by AddressSanitizer and
+UndefinedBehaviorSanitizer; the device code is built as usual. It is for CPU
+runs of the C-ABI tests only (load it with the sanitizer runtime preloaded,
+see ``HOSTSAN_RUNTIME``).
 """
 
 from __future__ import annotations
@@ -18,6 +25,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libfa_mi355x.so"
+HOSTSAN_LIB_NAME = "libfa_mi355x_hostsan.so"
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -32,22 +40,33 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+# host-only sanitizers: each -fsanitize= applies to the host compilation only
+HOSTSAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def hostsan_runtime() -> str | None:
+    """The AddressSanitizer runtime of the ROCm clang (to preload), or None."""
+    cands = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return cands[-1] if cands else None
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + (".hostsan.o" if sanitize else ".o"))
+    cmd = [HIPCC] + FLAGS + (HOSTSAN_FLAGS if sanitize else []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
-def build(verbose: bool = True) -> str:
+def build(verbose: bool = True, sanitize: bool = False) -> str:
     """Compile every HIP source and link the library; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
-        objs = list(ex.map(_compile, sources))
-    out = os.path.join(PKG, LIB_NAME)
+        objs = list(ex.map(lambda src: _compile(src, sanitize), sources))
+    out = os.path.join(PKG, HOSTSAN_LIB_NAME if sanitize else LIB_NAME)
     tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,4 +79,4 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build()
+    build(sanitize="--host-sanitize" in sys.argv[1:])

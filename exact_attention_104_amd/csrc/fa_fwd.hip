@@ -21,6 +21,8 @@
 // the other's products occupy the matrix core; K/V tiles arrive by direct
 // global->LDS loads into double buffers while the current tile is consumed,
 // with one barrier per tile.
+#include <atomic>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -35,9 +37,11 @@ namespace {
 // each wave still at two per SIMD): when every workgroup has only a few
 // tiles, one workgroup's loads, prologue and epilogue overlap another's
 // tiles, and under a mask the smaller Q-blocks split the uneven work more
-// evenly. Measured: faster up to 1024 keys without a mask and up to 4096
-// with one; slower beyond (the eight-wave blocks read each K/V tile from
-// HBM or L2 for twice as many rows).
+// evenly. These four-wave grids are persistent (see PERSIST below). Measured:
+// faster up to 1024 keys without a mask and up to 4096 with one, and at
+// d = 64 under a mask at every length; slower beyond at d = 128 (the
+// eight-wave blocks read each K/V tile from HBM or L2 for twice as many
+// rows).
 template <int D>
 constexpr int kNWof = D == 256 ? 4 : 8;
 constexpr int kQW = 32;   // query rows per wavefront
@@ -84,7 +88,16 @@ __device__ __forceinline__ void wait_loads_and_sync() {
 // are masked element by element. With ALiBi (kMaskBandAlibi) the scaled
 // score of query i and key j gets -slope_h |i + off - j|. kMaskNone and
 // kMaskCausal are the no-mask and plain causal bands with fixed arithmetic.
-template <int D, int MASK, int NW>
+//
+// PERSIST (the four-wave instances, short key ranges): the grid holds only as
+// many workgroups as fit on the chip at once, and each takes a contiguous run
+// of work items, one after another (a barrier between them, before the next
+// item's loads reuse the LDS buffers). With one workgroup per item, the
+// dispatcher starts items of mixed cost as slots free up and the slots sit
+// idle a third of the time at these lengths; contiguous runs give every
+// workgroup whole heads, i.e. the same mix of causal Q-block costs, and keep
+// a head's K / V within one workgroup's reach.
+template <int D, int MASK, int NW, bool PERSIST>
 __global__ void __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1)
 fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
            const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og, float* __restrict__ LSEg,
@@ -113,10 +126,26 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // round-robin over the 8 XCDs) so its K/V stay in that XCD's L2; inside a
   // head, the last Q-blocks (the heaviest under a causal band) go first.
   const int total = nqb * BH;
-  int wid = (int)blockIdx.x;
-  if ((total & 7) == 0) wid = (wid & 7) * (total >> 3) + (wid >> 3);
+  // Key tiles t0 .. t1 - 1 that hold the band of the rows of Q-block qblk.
+  auto block_tiles = [&](int qblk, int& t0, int& t1) __attribute__((always_inline)) {
+    const int q0 = qblk * kBR;
+    if constexpr (BAND) {
+      const int qlast = min(q0 + kBR, Nq) - 1;
+      const int blo = max(0, q0 + band.off - band.wl);
+      const int bhi = min(Nk - 1, qlast + band.off + band.wr);
+      t0 = blo / kBC;
+      t1 = bhi >= blo ? bhi / kBC + 1 : t0;
+    } else {
+      const int kend = CAUSAL ? min(Nk, q0 + kBR) : Nk;
+      t0 = 0;
+      t1 = (kend + kBC - 1) / kBC;
+    }
+  };
+  auto item_qblk = [&](int wid) { return MASK != kMaskNone ? nqb - 1 - (wid % nqb) : (wid % nqb); };
+  // One work item: Q-block item_qblk(wid) of head wid / nqb.
+  auto run_item = [&](int wid) __attribute__((always_inline)) {
   const int bh = wid / nqb;
-  const int qblk = MASK != kMaskNone ? nqb - 1 - (wid % nqb) : (wid % nqb);
+  const int qblk = item_qblk(wid);
   const int b = bh / H, h = bh % H, hk = h / group;  // query head h reads K/V head h / group
   const uint16_t* Qh = Qg + b * sq.b + h * sq.h;
   const uint16_t* Kh = Kg + b * sk.b + hk * sk.h;
@@ -127,13 +156,9 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
 
   // Key tiles t0 .. t1 - 1 hold the band of the block's rows; this wave's rows
   // need tiles wfirst .. wlast of them (none when its rows are all past Nq).
-  int t0 = 0, t1, wfirst = 0, wlast, klo = 0, khi = 0;
+  int t0, t1, wfirst = 0, wlast, klo = 0, khi = 0;
+  block_tiles(qblk, t0, t1);
   if constexpr (BAND) {
-    const int qlast = min(q0 + kBR, Nq) - 1;
-    const int blo = max(0, q0 + band.off - band.wl);
-    const int bhi = min(Nk - 1, qlast + band.off + band.wr);
-    t0 = blo / kBC;
-    t1 = bhi >= blo ? bhi / kBC + 1 : t0;
     const int wqlast = min(qw0 + kQW, Nq) - 1;
     const int wlo = max(0, qw0 + band.off - band.wl);
     const int whi = min(Nk - 1, wqlast + band.off + band.wr);
@@ -142,8 +167,6 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     klo = qrow + band.off - band.wl;  // this lane's visible keys
     khi = min(Nk - 1, qrow + band.off + band.wr);
   } else {
-    const int kend = CAUSAL ? min(Nk, q0 + kBR) : Nk;
-    t1 = (kend + kBC - 1) / kBC;
     wlast = CAUSAL ? min(t1 - 1, (qw0 + kQW - 1) / kBC) : t1 - 1;  // causal: the diagonal tile
   }
   float nslope = 0.f;  // ALiBi slope times log2 e, negated
@@ -153,6 +176,7 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     load_tile_async<D, false, NW>(sK0, Kh, sk.n, t0 * kBC, Nk, tid);
     load_tile_async<D, true, NW>(sV0, Vh, sv.n, t0 * kBC, Nk, tid);
   }
+
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[q][16 ks + 8 hi .. +7].
   bf16x8 qf[KS];
@@ -173,6 +197,24 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
 
   // One tile: K(t), V(t) are in (sK, sV); the loads of tile t+1 go to (nK, nV).
   const int lane_l32 = l32, lane_hi = hi, lane_g = g, lane_i16 = i16;
+  // Up to d = 128, the LDS byte offsets of this lane's operand reads inside a
+  // tile, computed once: the swizzles depend only on lane bits once the row
+  // offsets of the 32-key blocks and 16-key steps (multiples of 16 rows) are
+  // taken out, so every read in the tile is a buffer constant plus one of
+  // these (K: one per k-step; V^T: one per 32-row d block, the row 8 further
+  // down at a constant distance).
+  constexpr bool HOIST = D <= 128;
+  uint32_t koff[HOIST ? KS : 1], voff[HOIST ? DB : 1];
+  if constexpr (HOIST) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) koff[ks] = (uint32_t)(l32 * D + (((2 * ks + hi) ^ swz_k<D>(l32)) * 8)) * 2u;
+    const int rv = 4 * hi + (i16 >> 2);  // row of the V^T read within its 16-key step
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int d = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
+      voff[db] = (uint32_t)(rv * D + (((d >> 3) ^ swz_v<D>(rv)) * 8) + (d & 7)) * 2u;
+    }
+  }
   auto tile = [&](int t, const uint16_t* sK, const uint16_t* sV, uint16_t* nK, uint16_t* nV) {
     wait_loads_and_sync();  // tile t landed; every wave finished tile t-1
     if (t + 1 < t1) {
@@ -200,10 +242,14 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
     s[0] = f32x16{};
     s[1] = f32x16{};
     bf16x8 a[2], an[2];
+    const uint32_t kbase = lds_addr(sK), vbase = lds_addr(sV);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int r = kb * 32 + l32;
-      a[kb] = as_bf16x8(*(const u32x4*)(sK + r * D + ((hi ^ swz_k<D>(r)) * 8)));
+      if constexpr (HOIST)
+        a[kb] = as_bf16x8(lds_load16(kbase + kb * 32 * D * 2 + koff[0]));
+      else
+        a[kb] = as_bf16x8(*(const u32x4*)(sK + r * D + ((hi ^ swz_k<D>(r)) * 8)));
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -212,7 +258,10 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
         for (int kb = 0; kb < 2; ++kb) {
           const int r = kb * 32 + l32;
           const int c = (ks + 1) * 2 + hi;
-          an[kb] = as_bf16x8(*(const u32x4*)(sK + r * D + ((c ^ swz_k<D>(r)) * 8)));
+          if constexpr (HOIST)
+            an[kb] = as_bf16x8(lds_load16(kbase + kb * 32 * D * 2 + koff[ks + 1]));
+          else
+            an[kb] = as_bf16x8(*(const u32x4*)(sK + r * D + ((c ^ swz_k<D>(r)) * 8)));
         }
       }
 #pragma unroll
@@ -306,8 +355,15 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
         for (int db = 0; db < DB; ++db) {
           const int d = db * 32 + 16 * (g & 1) + 4 * (i16 & 3);
           const int c = d >> 3, within = d & 7;
-          const i16x4 t0 = lds_read_tr16(sV + r0 * D + ((c ^ swz_v<D>(r0)) * 8) + within);
-          const i16x4 t1 = lds_read_tr16(sV + r1 * D + ((c ^ swz_v<D>(r1)) * 8) + within);
+          i16x4 t0, t1;
+          if constexpr (HOIST) {
+            const uint32_t a0 = vbase + (kb * 32 + 16 * h2) * D * 2 + voff[db];
+            t0 = lds_read_tr16_at(a0);
+            t1 = lds_read_tr16_at(a0 + 8 * D * 2);
+          } else {
+            t0 = lds_read_tr16(sV + r0 * D + ((c ^ swz_v<D>(r0)) * 8) + within);
+            t1 = lds_read_tr16(sV + r1 * D + ((c ^ swz_v<D>(r1)) * 8) + within);
+          }
           const u32x4 au = {__builtin_bit_cast(u32x2, t0)[0], __builtin_bit_cast(u32x2, t0)[1],
                             __builtin_bit_cast(u32x2, t1)[0], __builtin_bit_cast(u32x2, t1)[1]};
           acc[db] = mfma_bf16_32x32x16(as_bf16x8(au), as_bf16x8(pb[kb][h2]), acc[db]);
@@ -340,15 +396,68 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       }
     if (hi == 0) LSEg[(size_t)bh * Nq + qrow] = lt > 0.f ? (m + __log2f(lt)) * kLn2 : -INFINITY;
   }
+  };  // run_item
+
+  if constexpr (PERSIST) {
+    // Items in falling cost (for a band: Q-block major, last block first),
+    // dealt in rounds of G = gridDim.x: even rounds to workgroups 0 .. G-1,
+    // odd rounds in reverse by groups of 8 (a workgroup keeps its place in
+    // its group of 8, i.e. its XCD, so a head's items stay on one XCD), which
+    // evens out the sums. Odd workgroups take their rounds from the last, so
+    // that workgroups sharing a CU are not in the same phase.
+    const int G = (int)gridDim.x, j = (int)blockIdx.x;
+    const int R = (total + G - 1) / G;
+    for (int k = 0; k < R; ++k) {
+      const int r = (j & 1) ? R - 1 - k : k;
+      const int jj = (r & 1) && (G & 7) == 0 ? ((G >> 3) - 1 - (j >> 3)) * 8 + (j & 7) : j;
+      const int i = r * G + jj;
+      if (i >= total) continue;
+      const int qb = MASK != kMaskNone ? i / BH : i % nqb;  // position in falling cost
+      const int bhh = MASK != kMaskNone ? i % BH : i / nqb;
+      const int wid = bhh * nqb + qb;  // run_item takes Q-block nqb - 1 - qb under a mask
+      run_item(wid);
+      __syncthreads();  // every wave is done with the LDS tiles before the next item's loads
+    }
+  } else {
+    int wid = (int)blockIdx.x;
+    if ((total & 7) == 0) wid = (wid & 7) * (total >> 3) + (wid >> 3);
+    run_item(wid);
+  }
+}
+
+// Workgroups of a kernel resident on the current device at once (CUs times
+// blocks per CU), looked up once per device and kernel.
+template <typename K>
+static int resident_slots(K kernel, int threads) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    v = per_cu * cus;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
 }
 
 template <int D, int MASK, int NW>
 static int launch_nw(const FwdArgs& a) {
   constexpr int kBR = NW * kQW;
+  constexpr bool PERSIST = D <= 128 && NW == 4;
   const int nqb = (a.Nq + kBR - 1) / kBR;
   const int BH = a.B * a.H;
-  const dim3 grid((unsigned)(nqb * BH)), block(NW * 64);
-  hipLaunchKernelGGL((fwd_kernel<D, MASK, NW>), grid, block, 0, (hipStream_t)a.stream,
+  int blocks = nqb * BH;
+  if constexpr (PERSIST) {
+    const int slots = resident_slots(fwd_kernel<D, MASK, NW, PERSIST>, NW * 64);
+    if (slots > 0 && blocks > slots) blocks = slots;
+  }
+  const dim3 grid((unsigned)blocks), block(NW * 64);
+  hipLaunchKernelGGL((fwd_kernel<D, MASK, NW, PERSIST>), grid, block, 0, (hipStream_t)a.stream,
                      a.q, a.k, a.v, a.o, a.lse, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.band,
                      a.slopes, a.sq, a.sk, a.sv, a.so);
   return hipGetLastError() == hipSuccess ? 0 : 1;
@@ -357,7 +466,8 @@ static int launch_nw(const FwdArgs& a) {
 template <int D, int MASK>
 static int launch(const FwdArgs& a) {
   if constexpr (kNWof<D> == 8) {
-    if (a.Nk <= (MASK == kMaskNone ? kShortKeys : kShortKeysMasked)) return launch_nw<D, MASK, 4>(a);
+    if (a.Nk <= (MASK == kMaskNone ? kShortKeys : kShortKeysMasked) || (D == 64 && MASK != kMaskNone))
+      return launch_nw<D, MASK, 4>(a);
   }
   return launch_nw<D, MASK, kNWof<D>>(a);
 }

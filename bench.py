@@ -368,7 +368,14 @@ def main():
                     help="with --only: run the timed kernel at sequence length SEQ and batch 16384 // SEQ "
                          "(the sweep's token count) instead of the headline shape, for profiling the short, "
                          "bandwidth-bound shapes")
+    ap.add_argument("--head-dim", type=int, default=None,
+                    help="with --only: run the timed kernel at this head dim (64 or 128) instead of 128")
     args = ap.parse_args()
+    if args.head_dim is not None:
+        if args.only is None or args.only.startswith("copy") or args.head_dim not in (64, 128):
+            ap.error("--head-dim profiles one kernel at d = 64 or 128: give --only as well")
+        global D
+        D = args.head_dim
     if args.seq is not None:
         if args.only is None or args.only.startswith("copy"):
             ap.error("--seq profiles one kernel: give --only fa_fwd, fa_bwd, fa_quant_fp8 or fa_fwd_fp8")

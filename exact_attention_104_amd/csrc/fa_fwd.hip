@@ -21,6 +21,7 @@
 // the other's products occupy the matrix core; K/V tiles arrive by direct
 // global->LDS loads into double buffers while the current tile is consumed,
 // with one barrier per tile.
+#include <algorithm>
 #include <atomic>
 
 #include "fa_device.h"
@@ -37,7 +38,7 @@ namespace {
 // each wave still at two per SIMD): when every workgroup has only a few
 // tiles, one workgroup's loads, prologue and epilogue overlap another's
 // tiles, and under a mask the smaller Q-blocks split the uneven work more
-// evenly. These four-wave grids are persistent (see PERSIST below). Measured:
+// evenly. These four-wave grids are persistent (see DEAL below). Measured:
 // faster up to 1024 keys without a mask and up to 4096 with one, and at
 // d = 64 under a mask at every length; slower beyond at d = 128 (the
 // eight-wave blocks read each K/V tile from HBM or L2 for twice as many
@@ -48,6 +49,9 @@ constexpr int kQW = 32;   // query rows per wavefront
 constexpr int kShortKeys = 1024;        // four-wave workgroups up to this many keys without a mask,
 constexpr int kShortKeysMasked = 4096;  // and up to this many under a mask
 constexpr int kBC = 64;   // keys per tile
+// Work dealing of the forward grid: one item per workgroup, or persistent
+// workgroups with a fixed list of items each (see the kernel).
+constexpr int kDealOne = 0, kDealFalling = 1, kDealByXcd = 2;
 #ifndef FA_RESCALE_SLACK
 #define FA_RESCALE_SLACK 8.0f
 #endif
@@ -89,15 +93,16 @@ __device__ __forceinline__ void wait_loads_and_sync() {
 // score of query i and key j gets -slope_h |i + off - j|. kMaskNone and
 // kMaskCausal are the no-mask and plain causal bands with fixed arithmetic.
 //
-// PERSIST (the four-wave instances, short key ranges): the grid holds only as
-// many workgroups as fit on the chip at once, and each takes a contiguous run
-// of work items, one after another (a barrier between them, before the next
-// item's loads reuse the LDS buffers). With one workgroup per item, the
-// dispatcher starts items of mixed cost as slots free up and the slots sit
-// idle a third of the time at these lengths; contiguous runs give every
-// workgroup whole heads, i.e. the same mix of causal Q-block costs, and keep
-// a head's K / V within one workgroup's reach.
-template <int D, int MASK, int NW, bool PERSIST>
+// DEAL: kDealOne launches one workgroup per item (one Q-block of one head).
+// The four-wave instances at d <= 128 (short key ranges) are persistent: the
+// grid holds only as many workgroups as fit on the chip at once, and each
+// runs a fixed list of items one after another (a barrier between them,
+// before the next item's loads reuse the LDS buffers). With one workgroup
+// per item the dispatcher starts items of mixed cost as slots free up and
+// the slots sit idle a third of the time at these lengths; the fixed lists
+// even out the causal costs, and kDealByXcd keeps the Q-blocks of a head
+// together in time on one XCD (kDealFalling where it cannot).
+template <int D, int MASK, int NW, int DEAL>
 __global__ void __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1)
 fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
            const uint16_t* __restrict__ Vg, uint16_t* __restrict__ Og, float* __restrict__ LSEg,
@@ -398,13 +403,28 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   }
   };  // run_item
 
-  if constexpr (PERSIST) {
-    // Items in falling cost (for a band: Q-block major, last block first),
-    // dealt in rounds of G = gridDim.x: even rounds to workgroups 0 .. G-1,
-    // odd rounds in reverse by groups of 8 (a workgroup keeps its place in
-    // its group of 8, i.e. its XCD, so a head's items stay on one XCD), which
-    // evens out the sums. Odd workgroups take their rounds from the last, so
-    // that workgroups sharing a CU are not in the same phase.
+  if constexpr (DEAL == kDealByXcd) {
+    // XCD x (workgroup j runs on XCD j % 8) takes heads x, x + 8, ..., and
+    // its G / 8 workgroups take them nqb items at a time, so all Q-blocks of
+    // a head run at once on one XCD and read each K / V tile from its L2 at
+    // about the same time. Odd rounds reverse the Q-block order inside each
+    // head, so that over two rounds every workgroup does one heavy and one
+    // light block under a causal band. The host picks this dealing only when
+    // every round holds whole heads (nqb divides G / 8) and every XCD as many
+    // heads (8 divides BH, G a multiple of 8).
+    const int j = (int)blockIdx.x, x = j & 7, s = j >> 3, Gx = (int)gridDim.x >> 3;
+    const int items = (BH >> 3) * nqb;  // items of this XCD
+    for (int u = s, k = 0; u < items; u += Gx, ++k) {
+      const int qb = (k & 1) ? nqb - 1 - u % nqb : u % nqb;
+      run_item(((u / nqb) * 8 + x) * nqb + qb);  // under a mask: Q-block nqb - 1 - qb
+      __syncthreads();  // every wave is done with the LDS tiles before the next item's loads
+    }
+  } else if constexpr (DEAL == kDealFalling) {
+    // Items in falling cost (Q-block major across heads under a mask), dealt
+    // in rounds of G: even rounds to workgroups 0 .. G-1, odd rounds in
+    // reverse by groups of 8 (a workgroup keeps its place in its group, i.e.
+    // its XCD), which evens out the sums; odd workgroups take their rounds
+    // from the last, so that workgroups sharing a CU are not in one phase.
     const int G = (int)gridDim.x, j = (int)blockIdx.x;
     const int R = (total + G - 1) / G;
     for (int k = 0; k < R; ++k) {
@@ -414,9 +434,8 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       if (i >= total) continue;
       const int qb = MASK != kMaskNone ? i / BH : i % nqb;  // position in falling cost
       const int bhh = MASK != kMaskNone ? i % BH : i / nqb;
-      const int wid = bhh * nqb + qb;  // run_item takes Q-block nqb - 1 - qb under a mask
-      run_item(wid);
-      __syncthreads();  // every wave is done with the LDS tiles before the next item's loads
+      run_item(bhh * nqb + qb);  // under a mask: Q-block nqb - 1 - qb
+      __syncthreads();
     }
   } else {
     int wid = (int)blockIdx.x;
@@ -425,10 +444,11 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   }
 }
 
-// Workgroups of a kernel resident on the current device at once (CUs times
-// blocks per CU), looked up once per device and kernel.
-template <typename K>
-static int resident_slots(K kernel, int threads) {
+// Workgroups of one kernel instance resident on the current device at once
+// (CUs times blocks per CU), looked up once per device and instance (the
+// cache is a static of the instance: all instances share one pointer type).
+template <int D, int MASK, int NW, int DEAL>
+static int resident_slots() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
   int dev = 0;
@@ -436,7 +456,8 @@ static int resident_slots(K kernel, int threads) {
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fwd_kernel<D, MASK, NW, DEAL>, NW * 64, 0) !=
+            hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
     v = per_cu * cus;
@@ -445,22 +466,30 @@ static int resident_slots(K kernel, int threads) {
   return v;
 }
 
+template <int D, int MASK, int NW, int DEAL>
+static int launch_deal(const FwdArgs& a, int nqb, int blocks) {
+  const dim3 grid((unsigned)blocks), block(NW * 64);
+  hipLaunchKernelGGL((fwd_kernel<D, MASK, NW, DEAL>), grid, block, 0, (hipStream_t)a.stream,
+                     a.q, a.k, a.v, a.o, a.lse, a.B * a.H, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.band,
+                     a.slopes, a.sq, a.sk, a.sv, a.so);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
 template <int D, int MASK, int NW>
 static int launch_nw(const FwdArgs& a) {
   constexpr int kBR = NW * kQW;
-  constexpr bool PERSIST = D <= 128 && NW == 4;
   const int nqb = (a.Nq + kBR - 1) / kBR;
   const int BH = a.B * a.H;
-  int blocks = nqb * BH;
-  if constexpr (PERSIST) {
-    const int slots = resident_slots(fwd_kernel<D, MASK, NW, PERSIST>, NW * 64);
-    if (slots > 0 && blocks > slots) blocks = slots;
+  const int blocks = nqb * BH;
+  if constexpr (D <= 128 && NW == 4) {  // persistent: at most one workgroup per resident slot
+    const int sx = resident_slots<D, MASK, NW, kDealByXcd>();
+    const int gx = sx > 0 ? std::min(blocks, sx) : blocks;
+    if (gx % 8 == 0 && BH % 8 == 0 && (gx / 8) % nqb == 0) return launch_deal<D, MASK, NW, kDealByXcd>(a, nqb, gx);
+    const int sf = resident_slots<D, MASK, NW, kDealFalling>();
+    return launch_deal<D, MASK, NW, kDealFalling>(a, nqb, sf > 0 ? std::min(blocks, sf) : blocks);
+  } else {
+    return launch_deal<D, MASK, NW, kDealOne>(a, nqb, blocks);
   }
-  const dim3 grid((unsigned)blocks), block(NW * 64);
-  hipLaunchKernelGGL((fwd_kernel<D, MASK, NW, PERSIST>), grid, block, 0, (hipStream_t)a.stream,
-                     a.q, a.k, a.v, a.o, a.lse, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale * kLog2e, a.band,
-                     a.slopes, a.sq, a.sk, a.sv, a.so);
-  return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
 template <int D, int MASK>

@@ -57,16 +57,60 @@ constexpr int kDealOne = 0, kDealFalling = 1, kDealByXcd = 2;
 #endif
 constexpr float kRescaleSlack = FA_RESCALE_SLACK;  // log2 units; P stays <= 256 in bf16
 
+// As lds_dma16 (fa_device.h), with the global address formed by the load
+// itself from a wave-uniform 64-bit base (SGPRs) plus this lane's 32-bit byte
+// offset, so that no per-lane 64-bit address arithmetic precedes it.
+// lds_wave_addr is the wave's LDS byte address (lane l lands at +16 l).
+__device__ __forceinline__ void lds_dma16_sbase(uint32_t lds_wave_addr, const void* sbase, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_addr);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(m0) : "memory");
+}
+
 // Direct global->LDS loads of one [64 x D] bf16 tile. Thread `tid` fills the
 // 16-byte LDS chunks n * 64 NW + tid of the tile; the source chunk is chosen
 // so that LDS holds the XOR-swizzled layout. Rows past the end are read from
 // row N-1 (finite values that are masked, or multiplied by P = 0).
+//
+// Up to d = 128 a thread's byte offsets (r rs + 8 c) 2 inside a tile are
+// formed once (TileLanes), and a full tile is loaded from the uniform base
+// head + k0 rs with those offsets: one load instruction per chunk and no
+// per-lane address arithmetic. That needs 64 rs 2 < 2^32 (row strides below
+// 2^25 elements); the last, ragged tile and larger strides take the general
+// form, which clamps each row and forms its 64-bit address.
+template <int D, bool IS_V, int NW>
+struct TileLanes {
+  static constexpr bool kOn = D <= 128;
+  static constexpr int kN = kOn ? (kBC * (D / 8)) / (NW * 64) : 1;
+  uint32_t off[kN];
+  __device__ __forceinline__ void init(long long rs, int tid) {
+    if constexpr (kOn) {
+      constexpr int CH = D / 8;
+#pragma unroll
+      for (int n = 0; n < kN; ++n) {
+        const int e = n * NW * 64 + tid;
+        const int r = e / CH, p = e % CH;
+        const int c = p ^ (IS_V ? swz_v<D>(r) : swz_k<D>(r));
+        off[n] = (uint32_t)(((uint64_t)r * (uint64_t)rs + (uint64_t)(c * 8)) * 2u);
+      }
+    }
+  }
+};
+
 template <int D, bool IS_V, int NW>
 __device__ __forceinline__ void load_tile_async(uint16_t* lds_tile, const uint16_t* head, long long rs, int k0,
-                                                int N, int tid) {
+                                                int N, int tid, const TileLanes<D, IS_V, NW>& tl, bool small_rs) {
   constexpr int CH = D / 8;
   const int w = tid >> 6;
   constexpr int kThreads = NW * 64;
+  if (TileLanes<D, IS_V, NW>::kOn && small_rs && k0 + kBC <= N) {
+    const uint16_t* base = head + (uint64_t)(uint32_t)k0 * (uint32_t)rs;  // the tile's first row
+    const uint32_t lds = lds_addr(lds_tile) + (uint32_t)__builtin_amdgcn_readfirstlane(w) * 1024u;
+#pragma unroll
+    for (int n = 0; n < TileLanes<D, IS_V, NW>::kN; ++n) lds_dma16_sbase(lds + n * kThreads * 16, base, tl.off[n]);
+    return;
+  }
 #pragma unroll
   for (int n = 0; n < (kBC * CH) / kThreads; ++n) {
     const int e = n * kThreads + tid;  // 16-byte chunk index inside the tile
@@ -131,6 +175,12 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   // round-robin over the 8 XCDs) so its K/V stay in that XCD's L2; inside a
   // head, the last Q-blocks (the heaviest under a causal band) go first.
   const int total = nqb * BH;
+  // lane offsets of the K / V tile loads, and whether the row strides allow them
+  TileLanes<D, false, NW> klanes;
+  TileLanes<D, true, NW> vlanes;
+  klanes.init(sk.n, tid);
+  vlanes.init(sv.n, tid);
+  const bool small_rs = sk.n < (1LL << 25) && sv.n < (1LL << 25);
   // Key tiles t0 .. t1 - 1 that hold the band of the rows of Q-block qblk.
   auto block_tiles = [&](int qblk, int& t0, int& t1) __attribute__((always_inline)) {
     const int q0 = qblk * kBR;
@@ -178,8 +228,8 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   if constexpr (ALIBI) nslope = -slopes[h] * kLog2e;
 
   if (t1 > t0) {
-    load_tile_async<D, false, NW>(sK0, Kh, sk.n, t0 * kBC, Nk, tid);
-    load_tile_async<D, true, NW>(sV0, Vh, sv.n, t0 * kBC, Nk, tid);
+    load_tile_async<D, false, NW>(sK0, Kh, sk.n, t0 * kBC, Nk, tid, klanes, small_rs);
+    load_tile_async<D, true, NW>(sV0, Vh, sv.n, t0 * kBC, Nk, tid, vlanes, small_rs);
   }
 
 
@@ -223,8 +273,8 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
   auto tile = [&](int t, const uint16_t* sK, const uint16_t* sV, uint16_t* nK, uint16_t* nV) {
     wait_loads_and_sync();  // tile t landed; every wave finished tile t-1
     if (t + 1 < t1) {
-      load_tile_async<D, false, NW>(nK, Kh, sk.n, (t + 1) * kBC, Nk, tid);
-      load_tile_async<D, true, NW>(nV, Vh, sv.n, (t + 1) * kBC, Nk, tid);
+      load_tile_async<D, false, NW>(nK, Kh, sk.n, (t + 1) * kBC, Nk, tid, klanes, small_rs);
+      load_tile_async<D, true, NW>(nV, Vh, sv.n, (t + 1) * kBC, Nk, tid, vlanes, small_rs);
     }
     if ((BAND && t < wfirst) || t > wlast) return;  // this wave's rows see none of these keys
     const int k0 = t * kBC;

@@ -138,3 +138,36 @@ def test_gqa_n8192_d128_sampled(gpu, causal):
         ek, ev = A.rel_rms(dk[0, hk, idx], rk), A.rel_rms(dv[0, hk, idx], rv)
         print("c%d dK/dV kv head %d rel_rms=%.3e %.3e" % (causal, hk, ek, ev), flush=True)
         assert ek <= GRAD_REL_RMS and ev <= GRAD_REL_RMS
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_row_stride_at_the_32_bit_offset_limit(gpu, d, causal):
+    """The forward loads full K / V tiles from the tile's first row plus a
+    32-bit per-lane byte offset while 64 row strides fit in 2^32 bytes (row
+    stride below 2^25 elements), and forms 64-bit addresses otherwise (and for
+    the ragged last tile). Q, K and V share rows of one buffer, with row
+    strides just below and at 2^25 elements (O, an output, may not overlap
+    them and has its own); N = 66 gives one full tile and a ragged one. Both
+    strides give the same bits, and both match the oracle."""
+    N, B, H = 66, 1, 1
+    x = fa_inputs.attention_inputs(B, H, N, d, seed=4400 + d + causal)
+    scale = 1.0 / math.sqrt(d)
+    ro, rl = A.forward(x["q"], x["k"], x["v"], causal, scale)
+    got = []
+    for rs in ((1 << 25) - 64, 1 << 25):
+        tag = "d%d c%d rs=%d" % (d, causal, rs)
+        print(tag, flush=True)
+        buf = torch.empty(N * rs, dtype=torch.bfloat16, device="cuda")  # N rows of rs elements
+        q, k, v = (buf.as_strided((B, H, N, d), (N * rs, N * rs, rs, 1), j * d) for j in range(3))
+        for t, n in zip((q, k, v), ("q", "k", "v")):
+            t.copy_(to_dev(x[n]))
+        o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+        o2, lse = gpu.fwd(q, k, v, causal=causal, out=o)
+        torch.cuda.synchronize()
+        assert o2.data_ptr() == o.data_ptr()
+        got.append((o.clone(), lse.clone()))
+        _check_fwd(o, lse, ro, rl, tag)
+        del buf, q, k, v, o, o2
+        torch.cuda.empty_cache()
+    assert torch.equal(got[0][0], got[1][0]) and torch.equal(got[0][1], got[1][1])

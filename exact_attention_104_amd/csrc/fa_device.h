@@ -97,6 +97,16 @@ __device__ __forceinline__ void lds_dma4(void* lds_wave_base, const void* src) {
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
                : "=&s"(saved) : "v"(src), "s"(m0) : "memory");
 }
+// As lds_dma16, with the global address formed by the load itself from a
+// wave-uniform 64-bit base (SGPRs) plus this lane's 32-bit byte offset, so
+// that no per-lane 64-bit address arithmetic precedes it. lds_wave_addr is the
+// wave's LDS byte address (lane l lands at +16 l).
+__device__ __forceinline__ void lds_dma16_sbase(uint32_t lds_wave_addr, const void* sbase, uint32_t voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_addr);
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(m0) : "memory");
+}
 // vmcnt(0), other counters untouched: every vector memory operation of this
 // wave, including the loads above, has completed.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }

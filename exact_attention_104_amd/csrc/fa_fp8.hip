@@ -172,12 +172,45 @@ constexpr float kF8Lazy = 3.f;        // rescale threshold (log2 units) of the r
 
 // Direct global->LDS loads of one [64 x D] e4m3 tile into the swizzled layout
 // of toff8 (rows past the end read row N-1; they are masked or meet P = 0),
-// 16-byte chunk i by thread i mod (64 NW), whole wavefronts at a time.
+// 16-byte chunk i by thread i mod (64 NW), whole wavefronts at a time. A
+// full tile is loaded from its first row (a uniform base) plus each lane's
+// byte offset inside the tile, formed once (tile8_offsets): no per-lane
+// address arithmetic per tile. The ragged last tile clamps each row. The
+// causal instances use this (FAST; 2.9% faster at N = 8192, d = 128); without
+// a mask it measured 1-2% slower, and those keep the per-row form.
 template <int D, int NW>
-__device__ __forceinline__ void load_tile8_async(uint8_t* lds_tile, const uint8_t* head, int k0, int N, int tid) {
+struct Tile8Lanes {
+  static constexpr int kN = (kF8BC * (D / 16) + NW * 64 - 1) / (NW * 64);
+  uint32_t off[kN];
+};
+template <int D, int NW>
+__device__ __forceinline__ Tile8Lanes<D, NW> tile8_offsets(int tid) {
+  constexpr int CHB = D / 16;
+  Tile8Lanes<D, NW> t;
+#pragma unroll
+  for (int n = 0; n < Tile8Lanes<D, NW>::kN; ++n) {
+    const int i = n * NW * 64 + tid;
+    const int r = i / CHB, p = i % CHB;
+    t.off[n] = (uint32_t)(r * D + (p ^ swz8<D>(r)) * 16);
+  }
+  return t;
+}
+template <int D, int NW, bool FAST>
+__device__ __forceinline__ void load_tile8_async(uint8_t* lds_tile, const uint8_t* head, int k0, int N, int tid,
+                                                 const Tile8Lanes<D, NW>& tl) {
   constexpr int CHB = D / 16;
   constexpr int CHUNKS = kF8BC * CHB;  // 512 (D = 128) or 256 (D = 64)
   constexpr int T = NW * 64;
+  if (FAST && k0 + kF8BC <= N) {
+    const uint8_t* base = head + (size_t)k0 * D;
+    const uint32_t lds = lds_addr(lds_tile) + (uint32_t)__builtin_amdgcn_readfirstlane(tid >> 6) * 1024u;
+#pragma unroll
+    for (int n = 0; n < Tile8Lanes<D, NW>::kN; ++n) {
+      if (CHUNKS - n * T < T && n * T + tid >= CHUNKS) return;  // whole wavefronts
+      lds_dma16_sbase(lds + n * T * 16, base, tl.off[n]);
+    }
+    return;
+  }
 #pragma unroll
   for (int i0 = 0; i0 < CHUNKS; i0 += T) {
     const int i = i0 + tid;
@@ -230,8 +263,10 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   const int ntiles = (kend + kF8BC - 1) / kF8BC;
   const int wlast = CAUSAL ? min(ntiles - 1, (qw0 + kF8QW - 1) / kF8BC) : ntiles - 1;
 
-  load_tile8_async<D, NW>(sK0, Kh, 0, N, tid);
-  load_tile8_async<D, NW>(sV0, Vh, 0, N, tid);
+  Tile8Lanes<D, NW> lanes8;  // used by the causal instances only
+  if constexpr (CAUSAL) lanes8 = tile8_offsets<D, NW>(tid);
+  load_tile8_async<D, NW, CAUSAL>(sK0, Kh, 0, N, tid, lanes8);
+  load_tile8_async<D, NW, CAUSAL>(sV0, Vh, 0, N, tid, lanes8);
 
   // R = 32 / max_j sv_j over the head: with the running max at most kF8Lazy
   // below a row's true maximum, every quantised p' = p sv_j R <= 32 * 8 = 256
@@ -357,8 +392,8 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
     wait_vmem_all();
     __syncthreads();  // tile t landed; every wave finished tile t-1
     if (!LAST && t + 1 < ntiles) {
-      load_tile8_async<D, NW>(nK, Kh, (t + 1) * kF8BC, N, tid);
-      load_tile8_async<D, NW>(nV, Vh, (t + 1) * kF8BC, N, tid);
+      load_tile8_async<D, NW, CAUSAL>(nK, Kh, (t + 1) * kF8BC, N, tid, lanes8);
+      load_tile8_async<D, NW, CAUSAL>(nV, Vh, (t + 1) * kF8BC, N, tid, lanes8);
     }
     if (t > wlast) return;
     const int k0 = t * kF8BC;

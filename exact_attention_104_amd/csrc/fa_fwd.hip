@@ -57,17 +57,6 @@ constexpr int kDealOne = 0, kDealFalling = 1, kDealByXcd = 2;
 #endif
 constexpr float kRescaleSlack = FA_RESCALE_SLACK;  // log2 units; P stays <= 256 in bf16
 
-// As lds_dma16 (fa_device.h), with the global address formed by the load
-// itself from a wave-uniform 64-bit base (SGPRs) plus this lane's 32-bit byte
-// offset, so that no per-lane 64-bit address arithmetic precedes it.
-// lds_wave_addr is the wave's LDS byte address (lane l lands at +16 l).
-__device__ __forceinline__ void lds_dma16_sbase(uint32_t lds_wave_addr, const void* sbase, uint32_t voff) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_addr);
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-               : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(m0) : "memory");
-}
-
 // Direct global->LDS loads of one [64 x D] bf16 tile. Thread `tid` fills the
 // 16-byte LDS chunks n * 64 NW + tid of the tile; the source chunk is chosen
 // so that LDS holds the XOR-swizzled layout. Rows past the end are read from

@@ -23,7 +23,7 @@ import torch
 import fa_inputs
 from oracle import attention as A
 from oracle import fp8 as F
-from gpu_util import FP8_O_REL_RMS, GRAD_REL_RMS, Guarded, to_dev, to_host
+from gpu_util import FP8_O_REL_RMS, GRAD_REL_RMS, LSE_ABS, O_MAX_ABS, Guarded, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -106,3 +106,38 @@ def test_fwd_fp8_outputs_covered(gpu, d, causal):
     e = A.rel_rms(to_host(go.t), r_o)
     print("fp8 guarded d%d c%d rel_rms=%.3e" % (d, causal, e), flush=True)
     assert e <= FP8_O_REL_RMS
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (4, 16, 2048, 64, True),     # persistent, head-major per XCD, two rounds (Q-block order flipped)
+    (16, 16, 1024, 128, True),   # persistent, head-major per XCD, four rounds
+    (16, 16, 1024, 128, False),  # the same without a mask
+    (5, 13, 2048, 64, True),     # B H not a multiple of 8: falling-cost dealing, two rounds
+    (7, 9, 2048, 128, True),     # the same at d = 128
+    (2, 16, 8192, 64, True),     # 64 Q-blocks per head do not divide the slots of an XCD: falling cost
+])
+def test_fwd_persistent_dealings_cover_outputs(gpu, B, H, N, d, causal):
+    """Each persistent dealing of the short-key forward writes every O and LSE
+    element once and nothing outside them, with results equal to a plain call
+    and, on sampled rows of the first and last heads, to the fp64 oracle."""
+    tag = "B%d H%d N%d d%d c%d" % (B, H, N, d, causal)
+    print(tag, flush=True)
+    x = fa_inputs.attention_inputs(B, H, N, d, seed=5100 + N + d + H)
+    q, k, v = (to_dev(x[n]) for n in ("q", "k", "v"))
+    go = Guarded((B, H, N, d), torch.bfloat16)
+    gl = Guarded((B, H, N), torch.float32)
+    gpu.fwd(q, k, v, causal=causal, out=go.t, lse=gl.t)
+    o2, l2 = gpu.fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    go.check(tag + " O")
+    gl.check(tag + " LSE")
+    assert torch.equal(go.t, o2) and torch.equal(gl.t, l2), tag
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, N - 2, N - 1],
+                                     np.random.default_rng(N).integers(0, N, 10)]))
+    o_h, l_h = to_host(go.t), to_host(gl.t)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        ro, rl = A.forward_head(x["q"][b, h], x["k"][b, h], x["v"][b, h], causal, 1.0 / math.sqrt(d), rows=rows)
+        e = np.abs(o_h[b, h, rows] - ro).max()
+        el = np.abs(l_h[b, h, rows] - rl).max()
+        print("%s head (%d,%d) O max_abs=%.3e LSE abs=%.3e" % (tag, b, h, e, el), flush=True)
+        assert e <= O_MAX_ABS and el <= LSE_ABS, (tag, b, h)

@@ -10,6 +10,9 @@
 // VGPRs (the key-stationary kernel wants the opposite).
 #include <type_traits>
 
+#include <algorithm>
+#include <atomic>
+
 #include "fa_bwd_tiles.h"
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -39,7 +42,14 @@ using namespace bwd;
 // Masks as in the forward (the band of keys i + off - wl .. i + off + wr of
 // 0 .. Nk - 1; kMaskBandAlibi adds -slope_h |i + off - j| to the scaled
 // scores; kMaskNone and kMaskCausal keep the fixed arithmetic).
-template <int D, int MASK, int NW>
+//
+// XCD: the grid holds one workgroup per resident slot, and XCD x (workgroup
+// j runs on XCD j % 8) takes heads x, x + 8, ..., its workgroups taking all
+// Q-blocks of a head at once, with the Q-block order reversed on odd rounds
+// (the forward's head-major dealing; the host uses it for the causal d = 128
+// instance when every round holds whole heads). Otherwise one workgroup per
+// (head, Q-block): the loop below then runs once.
+template <int D, int MASK, int NW, bool XCD = false>
 __global__ void __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1)
 dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
           const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
@@ -67,7 +77,17 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
   const int lane = tid & 63, w = BAND ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6, l32 = lane & 31,
             hi = lane >> 5;
 
-  const int wid = xcd_work_id(nqb * BH);
+  const int xj = (int)blockIdx.x, xx = xj & 7, xGx = (int)gridDim.x >> 3;
+  const int xitems = (BH >> 3) * nqb;  // items of this XCD (XCD dealing)
+  for (int xu = xj >> 3, xk = 0;; xu += xGx, ++xk) {
+  int wid;
+  if constexpr (XCD) {
+    if (xu >= xitems) break;
+    const int qb = (xk & 1) ? nqb - 1 - xu % nqb : xu % nqb;
+    wid = ((xu / nqb) * 8 + xx) * nqb + qb;  // under a mask: Q-block nqb - 1 - qb
+  } else {
+    wid = xcd_work_id(nqb * BH);
+  }
   const int bh = wid / nqb;
   const int qblk = MASK != kMaskNone ? nqb - 1 - (wid % nqb) : (wid % nqb);
   const int b = bh / H, h = bh % H, hk = h / group;  // query head h reads K/V head h / group
@@ -274,13 +294,48 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
         *(u32x2*)(row + d) = pk;
       }
   }
+  if constexpr (!XCD) break;
+  __syncthreads();  // every wave is done with the LDS tiles before the next item's loads
+  }  // items
+}
+
+// Workgroups of dq_kernel<D, MASK, NW, true> resident on the current device
+// at once, looked up once per device.
+template <int D, int MASK, int NW>
+static int dq_resident_slots() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dq_kernel<D, MASK, NW, true>, NW * 64, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    v = per_cu * cus;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
 }
 
 template <int D, int MASK, int NW>
 static int launch_dq_nw(const BwdArgs& a) {
   const int BH = a.B * a.H;
   const int nqb = (a.Nq + NW * 32 - 1) / (NW * 32);
-  hipLaunchKernelGGL((dq_kernel<D, MASK, NW>), dim3((unsigned)(nqb * BH)), dim3(NW * 64), 0, (hipStream_t)a.stream,
+  const int blocks = nqb * BH;
+  if constexpr (D == 128 && NW == 8 && MASK == kMaskCausal) {
+    const int slots = dq_resident_slots<D, MASK, NW>();
+    const int g = slots > 0 ? std::min(blocks, slots) : blocks;
+    if (g % 8 == 0 && BH % 8 == 0 && (g / 8) % nqb == 0) {
+      hipLaunchKernelGGL((dq_kernel<D, MASK, NW, true>), dim3((unsigned)g), dim3(NW * 64), 0, (hipStream_t)a.stream,
+                         a.q, a.k, a.v, a.dO, a.lse, a.delta, a.dq, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale,
+                         a.scale * kLog2e, a.band, a.slopes, a.sq, a.sk, a.sv, a.sdo, a.sdq);
+      return hipGetLastError() == hipSuccess ? 0 : 1;
+    }
+  }
+  hipLaunchKernelGGL((dq_kernel<D, MASK, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, (hipStream_t)a.stream,
                      a.q, a.k, a.v, a.dO, a.lse, a.delta, a.dq, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale,
                      a.scale * kLog2e, a.band, a.slopes, a.sq, a.sk, a.sv, a.sdo, a.sdq);
   return hipGetLastError() == hipSuccess ? 0 : 1;

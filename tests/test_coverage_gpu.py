@@ -141,3 +141,32 @@ def test_fwd_persistent_dealings_cover_outputs(gpu, B, H, N, d, causal):
         el = np.abs(l_h[b, h, rows] - rl).max()
         print("%s head (%d,%d) O max_abs=%.3e LSE abs=%.3e" % (tag, b, h, e, el), flush=True)
         assert e <= O_MAX_ABS and el <= LSE_ABS, (tag, b, h)
+
+
+def test_bwd_dq_persistent_dealing_covers_outputs(gpu):
+    """The causal d = 128 dQ kernel at N = 8192 runs a persistent grid, each
+    XCD taking all Q-blocks of a head per round (two rounds here, the second
+    in reversed Q-block order): every dQ element written once and nothing
+    outside it, equal to the unguarded call, and sampled rows of the first
+    and last heads against the fp64 oracle."""
+    B, H, N, d = 1, 16, 8192, 128
+    x = fa_inputs.attention_inputs(B, H, N, d, seed=5300, with_do=True)
+    dev = {n: to_dev(x[n]) for n in x}
+    o, lse = gpu.fwd(dev["q"], dev["k"], dev["v"], causal=True)
+    gq = Guarded((B, H, N, d), torch.bfloat16)
+    gk = Guarded((B, H, N, d), torch.bfloat16)
+    gv = Guarded((B, H, N, d), torch.bfloat16)
+    gpu.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True, out=(gq.t, gk.t, gv.t))
+    dq2, dk2, dv2 = gpu.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True)
+    torch.cuda.synchronize()
+    for name, g, ref in (("dQ", gq, dq2), ("dK", gk, dk2), ("dV", gv, dv2)):
+        g.check("n8192 " + name)
+        assert torch.equal(g.t, ref), name
+    rows = np.unique(np.concatenate([[0, 255, 256, 4095, 8191], np.random.default_rng(11).integers(0, N, 8)]))
+    got = to_host(gq.t)
+    for h in (0, H - 1):
+        ref = A.backward_head_rows(x["q"][0, h], x["k"][0, h], x["v"][0, h], x["do"][0, h], rows, True,
+                                   1.0 / math.sqrt(d))
+        e = A.rel_rms(got[0, h, rows], ref)
+        print("dQ head %d sampled rel_rms=%.3e" % (h, e), flush=True)
+        assert e <= GRAD_REL_RMS, h

@@ -64,6 +64,14 @@ def test_bwd_outputs_covered_plain(gpu, d, causal):
     _grads_guarded(gpu, 2, 3, 3, 777, 777, d, causal, None, 7100 + d)
 
 
+def test_bwd_outputs_covered_persistent_dkdv(gpu):
+    """Causal d = 128 with at most 1024 keys runs the dK / dV kernel on a
+    persistent grid (each XCD taking whole heads' key blocks per round, the
+    order reversed on odd rounds): 64 K/V heads, ragged N = 1000 (8 key
+    blocks), two rounds per workgroup."""
+    _grads_guarded(gpu, 4, 16, 16, 1000, 1000, 128, True, None, 7150)
+
+
 def test_bwd_outputs_covered_grouped_split(gpu):
     """H = 8 on H_kv = 2, short N: each key block's four query heads are split
     over workgroups that leave fp32 partials for the reduction kernel."""

@@ -178,3 +178,29 @@ def test_bwd_dq_persistent_dealing_covers_outputs(gpu):
         e = A.rel_rms(got[0, h, rows], ref)
         print("dQ head %d sampled rel_rms=%.3e" % (h, e), flush=True)
         assert e <= GRAD_REL_RMS, h
+
+
+def test_fwd_fp8_persistent_dealing_covers_outputs(gpu):
+    """Causal d = 128 fp8 forward on its persistent grid (each XCD taking all
+    Q-blocks of a head per round, four rounds, the order reversed on odd
+    rounds): O and LSE written once and nothing outside them; two heads
+    against the fp64 oracle on the dequantised inputs."""
+    B, H, N, d = 16, 16, 1024, 128
+    host = fa_inputs.attention_inputs(B, H, N, d, 7600, outliers=True)
+    dev = {n: to_dev(host[n]) for n in host}
+    qz = {n: gpu.quant_fp8(dev[n]) for n in ("q", "k", "v")}
+    go = Guarded((B, H, N, d), torch.bfloat16)
+    gl = Guarded((B, H, N), torch.float32)
+    gpu.fwd_fp8(qz["q"][0], qz["k"][0], qz["v"][0], qz["q"][1], qz["k"][1], qz["v"][1], causal=True,
+                out=go.t, lse=gl.t)
+    torch.cuda.synchronize()
+    go.check("fp8 persistent O")
+    gl.check("fp8 persistent LSE")
+    o_h = to_host(go.t)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        deq = {n: F.dequantize(qz[n][0][b:b + 1, h:h + 1].cpu().numpy(), qz[n][1][b:b + 1, h:h + 1].cpu().numpy())
+               for n in ("q", "k", "v")}
+        r_o, _ = A.forward(deq["q"], deq["k"], deq["v"], True, 1.0 / math.sqrt(d))
+        e = A.rel_rms(o_h[b:b + 1, h:h + 1], r_o)
+        print("fp8 persistent head (%d,%d) rel_rms=%.3e" % (b, h, e), flush=True)
+        assert e <= FP8_O_REL_RMS, (b, h)

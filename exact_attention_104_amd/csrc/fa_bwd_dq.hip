@@ -47,7 +47,9 @@ using namespace bwd;
 // j runs on XCD j % 8) takes heads x, x + 8, ..., its workgroups taking all
 // Q-blocks of a head at once, with the Q-block order reversed on odd rounds
 // (the forward's head-major dealing; the host uses it for the causal d = 128
-// instance when every round holds whole heads). Otherwise one workgroup per
+// instances, four or eight waves, when every round holds whole heads; the
+// four-wave one spills 24 VGPRs there and is still 1-2% faster at
+// N = 1024 - 4096). Otherwise one workgroup per
 // (head, Q-block): the loop below then runs once.
 template <int D, int MASK, int NW, bool XCD = false>
 __global__ void __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1)
@@ -325,7 +327,7 @@ static int launch_dq_nw(const BwdArgs& a) {
   const int BH = a.B * a.H;
   const int nqb = (a.Nq + NW * 32 - 1) / (NW * 32);
   const int blocks = nqb * BH;
-  if constexpr (D == 128 && NW == 8 && MASK == kMaskCausal) {
+  if constexpr (D == 128 && MASK == kMaskCausal) {
     const int slots = dq_resident_slots<D, MASK, NW>();
     const int g = slots > 0 ? std::min(blocks, slots) : blocks;
     if (g % 8 == 0 && BH % 8 == 0 && (g / 8) % nqb == 0) {

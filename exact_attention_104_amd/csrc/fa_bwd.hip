@@ -85,8 +85,12 @@ pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, floa
 // a light one and the key blocks of a head read the same Q / dO tiles at
 // about the same time. Otherwise one workgroup per key block: the loop below
 // then runs once.
+//
+// Up to d = 64 a wave fits in 256 VGPRs with no AGPRs (two workgroups per
+// CU). The launch bound says so: the compiler then gives every MFMA its VGPR
+// form, and S and dP need no copies out of AGPRs before the vector work.
 template <int D, int MASK, bool XCD = false>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, D <= 64 ? 2 : 1)
 dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
             const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
             uint16_t* __restrict__ dKg, uint16_t* __restrict__ dVg, float* __restrict__ part, int BHkv, int H,
@@ -318,15 +322,24 @@ dkdv_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, co
     dk[db] = mfma_bf16_32x32x16(as_bf16x8(pS[s2]), as_bf16x8(bq), dk[db]);
   };
   // Register placement: the loop-invariant K / V operands and the dK / dV
-  // accumulators are pinned to AGPRs at the loop boundaries (an MFMA reads its
-  // B operand and accumulator there directly). Left to itself the compiler
-  // moved the accumulators through VGPRs on every step and kept no VGPRs free
-  // for reading LDS ahead.
+  // accumulators are pinned at the loop boundaries. Above d = 64 they go to
+  // AGPRs (an MFMA reads its B operand and accumulator there directly); left
+  // to itself the compiler moved the accumulators through VGPRs on every step
+  // and kept no VGPRs free for reading LDS ahead. Up to d = 64 everything
+  // stays in VGPRs (an AGPR constraint would switch every MFMA of the kernel
+  // to its AGPR form and bring back the copies of S and dP).
   auto pin_acc = [&]() __attribute__((always_inline)) {
+    if constexpr (D <= 64) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+v"(dk[db]), "+v"(dv[db]));
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(kf[ks]), "+v"(vf[ks]));
+    } else {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) asm volatile("" : "+a"(dk[db]), "+a"(dv[db]));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
+    }
   };
 
   // ALiBi slope (negated, times log2 e) of the query head of a step

@@ -364,8 +364,14 @@ fwd_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg,
       const float m_new = fmaxf(m, mx);
       const float alpha = fast_exp2(m - m_new);
       l *= alpha;
+      // At d = 256, O^T lives in AGPRs. The pin keeps the copies out to VGPRs
+      // (and back) that the multiply needs inside this rarely taken branch;
+      // without it the compiler read all 128 registers out on every tile.
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      for (int db = 0; db < DB; ++db) {
+        if constexpr (D == 256) asm volatile("" : "+a"(acc[db]));
+        acc[db] *= alpha;
+      }
       m = m_new;
     }
     float rs4[4] = {0.f, 0.f, 0.f, 0.f};  // row sum in four chains (shorter dependences)

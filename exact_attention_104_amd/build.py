@@ -40,6 +40,11 @@ FLAGS = [
 ]
 
 
+# per-file additions: the d = 256 backward is built with every MFMA in its VGPR
+# form (its dK/dV kernel then keeps S and dP out of AGPRs; the flag acts on a
+# whole file and slowed the d = 128 instances, hence a file of its own)
+FILE_FLAGS = {"fa_bwd_d256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 # host-only sanitizers: each -fsanitize= applies to the host compilation only
 HOSTSAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
                  "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
@@ -53,7 +58,8 @@ def hostsan_runtime() -> str | None:
 
 def _compile(src: str, sanitize: bool = False) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + (".hostsan.o" if sanitize else ".o"))
-    cmd = [HIPCC] + FLAGS + (HOSTSAN_FLAGS if sanitize else []) + ["-c", src, "-o", obj]
+    extra = FILE_FLAGS.get(os.path.basename(src), [])
+    cmd = [HIPCC] + FLAGS + extra + (HOSTSAN_FLAGS if sanitize else []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -494,7 +494,7 @@ def main():
     if peak:
         achieved = breakdown[name]["tflops"]
         traffic = None
-        if name == "fa_bwd":  # one C-ABI launch: pre_kernel, dkdv_kernel, dq_kernel
+        if name == "fa_bwd":  # one C-ABI call: dq_kernel (which also forms D), dkdv_kernel
             traffic = measured_traffic(os.path.join(ROOT, "profiles", "fa_bwd_n8192_d128_causal_hbm_bytes.md"))
         roofline = {"kernel": name, "bound": "mfma", "achieved": achieved, "peak": peak,
                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic,

@@ -6,8 +6,12 @@
 // of the forward definition: dV = P^T dO, dP = dO V^T, D = rowsum(dO o O),
 // dS = P o (dP - D), dQ = scale dS K, dK = scale dS^T Q.
 //
-// Three launches on the caller's stream, none with atomics:
-//   1. pre_kernel  : D = rowsum(dO o O) in fp32.
+// Two launches on the caller's stream, none with atomics:
+//   1. dq_kernel   : (fa_bwd_dq.hip) one workgroup per (batch, head, 256-row Q
+//                    block) streaming K / V tiles: S^T, dP^T, dS^T, then
+//                    dQ^T += K^T dS^T. Each wave first forms D = rowsum(dO o O)
+//                    of its 32 rows in fp32 (it holds their dO already) and
+//                    writes it to the workspace for the next launch.
 //   2. dkdv_kernel : one workgroup per (batch, head, 128-key block); four waves
 //                    own 32 keys each and keep K, V (MFMA operands) and the dK,
 //                    dV accumulators in registers for the whole pass. For every
@@ -17,9 +21,6 @@
 //                    that one block's dV / dK products overlap the next
 //                    block's P / dS work. The next blocks' tiles arrive by
 //                    direct global->LDS loads meanwhile.
-//   3. dq_kernel   : (fa_bwd_dq.hip) one workgroup per (batch, head, 256-row Q
-//                    block) streaming K / V tiles: S^T, dP^T, dS^T, then
-//                    dQ^T += K^T dS^T.
 // Splitting dQ from dK/dV recomputes S and dP once more (7 instead of 5
 // matrix products) but needs no fp32 atomics: on this chip an fp32 atomic add
 // retires about ten times slower than a store, and one dQ partial per

@@ -1,9 +1,10 @@
-// dQ of the bf16 attention backward (third launch of fa_bwd; the method and
-// the first two launches are described in fa_bwd.hip).
+// dQ of the bf16 attention backward (first launch of fa_bwd; the method and
+// the second launch are described in fa_bwd.hip).
 //
 // One workgroup per (batch, head, 256-row Q block): eight waves of 32 query
-// rows keep Q and dO (MFMA operands) and the dQ accumulator in registers and
-// stream 64-key K / V tiles: S^T = K Q^T and dP^T = V dO^T (lane = query),
+// rows keep Q and dO (MFMA operands) and the dQ accumulator in registers,
+// form D = rowsum(dO o O) of their rows (written to the workspace for the
+// dK/dV launch that follows), and stream 64-key K / V tiles: S^T = K Q^T and dP^T = V dO^T (lane = query),
 // P = exp2(S c - L log2 e) and dS = P o (dP - D) lane-locally, then
 // dQ^T += K^T dS^T with K read transposed ([HUB] "How it works": dQ = scale
 // dS K). Kept in its own file because it compiles best with MFMAs that write
@@ -48,16 +49,16 @@ using namespace bwd;
 // Q-blocks of a head at once, with the Q-block order reversed on odd rounds
 // (the forward's head-major dealing; the host uses it for the causal d = 128
 // instances, four or eight waves, when every round holds whole heads; the
-// four-wave one spills 24 VGPRs there and is still 1-2% faster at
+// four-wave one spills 29 VGPRs there and is still 1-2% faster at
 // N = 1024 - 4096). Otherwise one workgroup per
 // (head, Q-block): the loop below then runs once.
 template <int D, int MASK, int NW, bool XCD = false>
 __global__ void __launch_bounds__(NW * 64, (D <= 128 && NW == 4) ? 2 : 1)
 dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, const uint16_t* __restrict__ Vg,
-          const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, const float* __restrict__ Dg,
-          uint16_t* __restrict__ dQg, int BH, int H, int group, int Nq, int Nk, int nqb, float scale,
-          float scale_log2, Band band, const float* __restrict__ slopes, Strides sq, Strides sk, Strides sv,
-          Strides sdo, Strides sdq) {
+          const uint16_t* __restrict__ dOg, const float* __restrict__ LSEg, const uint16_t* __restrict__ Og,
+          float* __restrict__ Dg, uint16_t* __restrict__ dQg, int BH, int H, int group, int Nq, int Nk, int nqb,
+          float scale, float scale_log2, Band band, const float* __restrict__ slopes, Strides sq, Strides sk,
+          Strides sv, Strides sdo, Strides so, Strides sdq) {
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = kQBC * D;
@@ -141,7 +142,22 @@ dq_kernel(const uint16_t* __restrict__ Qg, const uint16_t* __restrict__ Kg, cons
   // rows past Nq: L = +inf gives P = 0 (rows that see no key have L = -inf and
   // lie only in masked tiles, where P is set to 0)
   const float Lq = qrow < Nq ? LSEg[(size_t)bh * Nq + qrow] * kLog2e : INFINITY;
-  const float Dq = qrow < Nq ? Dg[(size_t)bh * Nq + qrow] : 0.f;
+  // D = rowsum(dO o O) of this lane's row, from the half row of dO it holds
+  // (lanes l and l + 32 hold the two halves); written for the dK/dV kernel,
+  // which runs after this one
+  float dpart = 0.f;
+  if (qrow < Nq) {
+    const uint16_t* orow = Og + b * so.b + h * so.h + (size_t)qrow * so.n + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 o = *(const u32x4*)(orow + ks * 16);
+      const u32x4 e = __builtin_bit_cast(u32x4, of[ks]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dpart += bf16_lo(o[j]) * bf16_lo(e[j]) + bf16_hi(o[j]) * bf16_hi(e[j]);
+    }
+  }
+  const float Dq = dpart + __shfl_xor(dpart, 32);
+  if (hi == 0 && qrow < Nq) Dg[(size_t)bh * Nq + qrow] = Dq;
 
   f32x16 acc[DB];
 #pragma unroll
@@ -332,14 +348,14 @@ static int launch_dq_nw(const BwdArgs& a) {
     const int g = slots > 0 ? std::min(blocks, slots) : blocks;
     if (g % 8 == 0 && BH % 8 == 0 && (g / 8) % nqb == 0) {
       hipLaunchKernelGGL((dq_kernel<D, MASK, NW, true>), dim3((unsigned)g), dim3(NW * 64), 0, (hipStream_t)a.stream,
-                         a.q, a.k, a.v, a.dO, a.lse, a.delta, a.dq, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale,
-                         a.scale * kLog2e, a.band, a.slopes, a.sq, a.sk, a.sv, a.sdo, a.sdq);
+                         a.q, a.k, a.v, a.dO, a.lse, a.o, a.delta, a.dq, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale,
+                         a.scale * kLog2e, a.band, a.slopes, a.sq, a.sk, a.sv, a.sdo, a.so, a.sdq);
       return hipGetLastError() == hipSuccess ? 0 : 1;
     }
   }
   hipLaunchKernelGGL((dq_kernel<D, MASK, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, (hipStream_t)a.stream,
-                     a.q, a.k, a.v, a.dO, a.lse, a.delta, a.dq, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale,
-                     a.scale * kLog2e, a.band, a.slopes, a.sq, a.sk, a.sv, a.sdo, a.sdq);
+                     a.q, a.k, a.v, a.dO, a.lse, a.o, a.delta, a.dq, BH, a.H, a.H / a.Hkv, a.Nq, a.Nk, nqb, a.scale,
+                     a.scale * kLog2e, a.band, a.slopes, a.sq, a.sk, a.sv, a.sdo, a.so, a.sdq);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

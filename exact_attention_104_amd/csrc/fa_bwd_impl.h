@@ -25,28 +25,6 @@ constexpr int kKeyBlocksPersistent = 8;  // dkdv: persistent grid up to this man
 
 using namespace bwd;
 
-template <int D>
-__global__ void __launch_bounds__(256)
-pre_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, float* __restrict__ delta,
-           long long rows, int H, int N, Strides so, Strides sdo) {
-  constexpr int LPR = D / 8;        // lanes per row, 8 elements each
-  constexpr int RPB = 256 / LPR;    // rows per block
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
-  const int c = threadIdx.x % LPR;
-  float s = 0.f;
-  if (row < rows) {
-    const long long bh = row / N;
-    const int n = (int)(row % N), b = (int)(bh / H), h = (int)(bh % H);
-    const u32x4 a = *(const u32x4*)(O + b * so.b + h * so.h + (long long)n * so.n + c * 8);
-    const u32x4 e = *(const u32x4*)(dO + b * sdo.b + h * sdo.h + (long long)n * sdo.n + c * 8);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s += bf16_lo(a[j]) * bf16_lo(e[j]) + bf16_hi(a[j]) * bf16_hi(e[j]);
-  }
-#pragma unroll
-  for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
-  if (row < rows && c == 0) delta[row] = s;
-}
-
 // ---------------------------------------------------------------------------
 // dK, dV: key-stationary
 // ---------------------------------------------------------------------------
@@ -511,10 +489,10 @@ kv_reduce_kernel(const float* __restrict__ part, uint16_t* __restrict__ dKg, uin
 template <int D, int MASK>
 static int launch(const BwdArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
-  const long long rows = (long long)a.B * a.H * a.Nq;
   constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((pre_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, st, a.o, a.dO,
-                     a.delta, rows, a.H, a.Nq, a.so, a.sdo);
+  // dQ first: its kernel also forms D = rowsum(dO o O) of every query row and
+  // writes it to the workspace, where the dK/dV kernel reads it
+  if (launch_bwd_dq(a) != 0) return 1;
   const int nkb = bwd_key_blocks(a.Nk);
   static_assert(kBKC == 128, "bwd_key_blocks assumes 128-key blocks");
   const int BHkv = a.B * a.Hkv;
@@ -549,7 +527,7 @@ static int launch(const BwdArgs& a) {
                        a.part, a.dk, a.dv, kv_rows, a.Hkv, a.split, a.Nk, a.scale, a.sdk, a.sdv);
     if (hipGetLastError() != hipSuccess) return 1;
   }
-  return launch_bwd_dq(a);
+  return 0;
 }
 
 template <int D>

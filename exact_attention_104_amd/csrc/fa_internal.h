@@ -99,7 +99,7 @@ struct Fp8FwdArgs {
 int launch_fwd(const FwdArgs& a);
 int launch_bwd(const BwdArgs& a);     // all three backward launches
 int launch_bwd_d256(const BwdArgs& a);  // the same at d = 256 (fa_bwd_d256.hip)
-int launch_bwd_dq(const BwdArgs& a);  // the dQ launch alone (after D is written)
+int launch_bwd_dq(const BwdArgs& a);  // the dQ launch (it also writes D for the dK/dV launch)
 int launch_quant_fp8(const QuantArgs& a);
 int launch_fwd_fp8(const Fp8FwdArgs& a);
 

@@ -131,6 +131,14 @@ def backward_head(q, k, v, do, causal: bool, scale: float):
     return dq, dk, dv
 
 
+def row_delta(o, do) -> np.ndarray:
+    """D_i = sum_d dO_id O_id in float64, over the last axis. It is the row term
+    of dS = P * (dP - D): with O = P V, sum_d dO_id O_id = sum_j P_ij dP_ij
+    (the chain rule through the softmax; the pages only say that the backward
+    recomputes P). The kernels form D from their own bf16 O."""
+    return (_f64(do) * _f64(o)).sum(axis=-1)
+
+
 def backward(q, k, v, do, causal: bool = False, scale: float | None = None):
     """Backward for ``[B, H, N, d]`` inputs: returns (dQ, dK, dV) in float64."""
     q, k, v, do = (_f64(x) for x in (q, k, v, do))

@@ -84,3 +84,30 @@ def test_bwd_deterministic(gpu):
     dq2, dk2, dv2 = gpu.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(dk, dk2) and torch.equal(dv, dv2) and torch.equal(dq, dq2)
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [
+    (1, 2, 300, 64, False),
+    (1, 2, 300, 128, True),
+    (1, 2, 257, 256, True),
+    (2, 16, 1024, 128, True),  # the persistent four-wave dQ instance
+    (2, 16, 8192, 128, True),  # the headline shape: the persistent eight-wave instance
+])
+def test_bwd_row_delta_in_workspace(gpu, B, H, N, d, causal):
+    """Row term D = rowsum(dO o O) of every query row, formed by the dQ kernel
+    from the kernel's own bf16 O and left in the caller's workspace (filled
+    with NaN bytes beforehand), against the oracle's row_delta. The products
+    of two bf16 values are exact in fp32, so the only error is the fp32 sum."""
+    host, dev = inputs_on_device(B, H, N, d, 40 + N, with_do=True)
+    o, lse = gpu.fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+    ws = torch.full((gpu.bwd_workspace_bytes(B, H, N, d),), 0xFF, dtype=torch.uint8, device="cuda")
+    gpu.bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, causal=causal, workspace=ws)
+    torch.cuda.synchronize()
+    got = ws[: B * H * N * 4].view(torch.float32).reshape(B, H, N).cpu().numpy().astype(np.float64)
+    o_host = to_host(o)
+    ref = A.row_delta(o_host, host["do"])
+    bound = np.abs(o_host * host["do"]).sum(axis=-1)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref)
+    print("D max_abs=%.3e max_rel_to_sum_abs=%.3e" % (err.max(), (err / np.maximum(bound, 1e-30)).max()), flush=True)
+    assert (err <= 1e-5 * bound + 1e-30).all()

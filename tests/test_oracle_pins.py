@@ -9,6 +9,7 @@ Pin list (each test names what it pins):
   P-5 finite differences of L = sum(O * dO) match the analytic gradients
   P-6 torch SDPA (CPU, float64) and torch.autograd agree with O, dQ, dK, dV
   P-7 special cases (N = 1, causal row 0, V shift / scale, key permutation)
+  P-8 D = rowsum(dO o O) equals rowsum(P o dP) when O = P V (and a closed form)
   G-1 hand-derived closed-form example (tests/golden/tiny_closed_form.json)
   Planted mistakes: each plausible bug in the oracle fails at least one pin.
 """
@@ -261,6 +262,22 @@ def test_metrics():
     assert A.max_abs(ref + np.array([0.3, -0.5]), ref) == pytest.approx(0.5)
 
 
+def pin_row_delta(causal):
+    """D from O and dO equals sum_j P_ij dP_ij computed from P and dP = dO V^T,
+    which is how the chain rule reaches it; plus a hand-computed case."""
+    q, k, v, do = (_rand((29, 8), s) for s in (21, 22, 23, 24))
+    o, _ = A.forward_head(q, k, v, causal, 0.3)
+    p = A.probabilities(q, k, causal, 0.3)
+    ref = (p * (do @ v.T)).sum(axis=1)
+    assert np.allclose(A.row_delta(o, do), ref, rtol=1e-12, atol=1e-12)
+    assert A.row_delta(np.array([[1.0, 2.0], [0.5, -1.0]]), np.array([[3.0, 4.0], [2.0, 2.0]])).tolist() == [11.0, -1.0]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_p8_row_delta(causal):
+    pin_row_delta(causal)
+
+
 # ------------------------------------------------------------------ planted mistakes
 def _mask_off_by_one(q, k, scale, causal, rows=None):
     """Causal mask that lets each query see one key too many."""
@@ -313,6 +330,16 @@ def _expand_kv_modulo(x, H):
     return np.tile(x, (1, H // x.shape[1], 1, 1))
 
 
+def _row_delta_over_rows(o, do):
+    """Wrong axis: sums dO o O over the rows instead of along d."""
+    return (np.asarray(do, np.float64) * np.asarray(o, np.float64)).sum(axis=0)
+
+
+def _row_delta_o_squared(o, do):
+    """Wrong operand: sums O o O along d."""
+    return (np.asarray(o, np.float64) ** 2).sum(axis=-1)
+
+
 def _backward_gqa_first_head(q, k, v, do, causal=False, scale=None):
     """Forgets the group sum: keeps only the first query head's dK, dV."""
     B, H, N, d = q.shape
@@ -330,6 +357,8 @@ def _backward_gqa_first_head(q, k, v, do, causal=False, scale=None):
     ("backward_head", _backward_transposed, ["fd", "sdpa"]),
     ("backward_head", _backward_no_scale, ["fd", "sdpa"]),
     ("safe_softmax_rows", _softmax_no_log, ["lse", "zero_query", "golden"]),
+    ("row_delta", _row_delta_over_rows, ["row_delta"]),
+    ("row_delta", _row_delta_o_squared, ["row_delta"]),
 ])
 def test_planted_mistakes_are_caught(monkeypatch, target, replacement, pins):
     """Each planted bug (in the oracle, on the CPU) must fail every listed pin."""
@@ -346,6 +375,7 @@ def test_planted_mistakes_are_caught(monkeypatch, target, replacement, pins):
         "golden": pin_golden_closed_form,
         "golden_scale": lambda: pin_torch_sdpa(False, n=9, d=4),
         "sdpa_gqa": lambda: pin_torch_sdpa_gqa(True, n=9, d=4),
+        "row_delta": lambda: pin_row_delta(True),
     }
     for name in pins:
         with pytest.raises((AssertionError, ValueError, FloatingPointError)):

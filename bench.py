@@ -285,6 +285,38 @@ def widened(fa, dev, q, k, v, do, steps=10, warmup=5):
     return out
 
 
+def fp8_exp_modes(fa, q8, k8, v8, qs, ks, vs, flops, rounds=10, warmup=3):
+    """The fp8 forward with its softmax exponentials on the hardware unit
+    (exp_mode 0, the step's form) and in the software 2^x for one in four
+    (1) or all (2) of them: the three modes interleaved call by call, so each
+    sees the same clock, each timed with HIP events on the current stream."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    fns = [lambda m=m: fa.fwd_fp8(q8, k8, v8, qs, ks, vs, causal=True, exp_mode=m) for m in range(3)]
+    for _ in range(warmup):
+        for fn in fns:
+            fn()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in fns]
+           for _ in range(rounds)]
+    torch.cuda.synchronize()
+    for r in range(rounds):
+        for i, fn in enumerate(fns):
+            evs[r][i][0].record(stream)
+            fn()
+            evs[r][i][1].record(stream)
+    torch.cuda.synchronize()
+    out = {}
+    for i in range(3):
+        st = call_stats([evs[r][i][0].elapsed_time(evs[r][i][1]) for r in range(rounds)])
+        st["tflops"] = flops / (st["ms_median"] * 1e-3) / 1e12
+        st["frac"] = st["tflops"] / PEAK_FP8
+        out["exp_mode%d" % i] = st
+        log("fp8 exp_mode %d: %.3f ms (%.3f..%.3f) %.0f TFLOP/s"
+            % (i, st["ms_median"], st["ms_min"], st["ms_max"], st["tflops"]))
+    return out
+
+
 def sweep(fa, dev, steps=10, warmup=5):
     """Sequence-length sweep at a fixed token count: N = 512 .. 16384 with
     B = 16384 / N, H = 16, d = 64 and 128, causal and not; forward and backward
@@ -551,6 +583,9 @@ def main():
     wid = None
     if not args.no_widened and args.only is None and have_bwd:
         wid = widened(fa, dev, q, k, v, do)
+    f8x = None
+    if not args.no_widened and args.only is None and have_f8:
+        f8x = fp8_exp_modes(fa, q8, k8, v8, qs, ks, vs, fwd_flops(B, H, N, D))
     swp = None
     if not args.no_sweep and args.only is None and have_bwd:
         swp = sweep(fa, dev)
@@ -587,6 +622,7 @@ def main():
         "cpu_baseline": cpu,
         "context": {"library_bf16_gemm": gemm},
         "widened": wid,  # each row: median of 10 calls, with min / max
+        "fp8_exp_modes": f8x,  # software 2^x in the fp8 forward's softmax: none, 1 in 4, all
         "sweep": swp,
     }
     print(json.dumps(out), flush=True)

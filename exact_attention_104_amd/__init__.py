@@ -66,6 +66,7 @@ SIGNATURES = {
     "fa_bwd_ext": (_I, [_P] * 9 + [_I] * 6 + [_P, _P, _F, _P, ctypes.c_size_t, _P]),
     "fa_quant_fp8": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "fa_fwd_fp8": (_I, [_P] * 8 + [_I, _I, _I, _I, _I, _F, _P]),
+    "fa_fwd_fp8_ext": (_I, [_P] * 8 + [_I, _I, _I, _I, _I, _F, _I, _P]),
 }
 
 
@@ -303,9 +304,11 @@ def quant_fp8(x, signs=None):
 
 
 def fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: float | None = None,
-            out=None, lse=None):
+            out=None, lse=None, exp_mode: int = 0):
     """fp8 forward on quantised inputs: returns (O bf16, LSE fp32); out / lse
-    are optional caller-owned contiguous outputs."""
+    are optional caller-owned contiguous outputs. exp_mode 1 (2) computes one
+    in four (all) of the softmax exponentials with the software 2^x
+    (fa_fwd_fp8_ext; d = 128 only); 0 uses the hardware exponential."""
     lib = load_library()
     B, H, N, d = _bhnd(q8)
     nb = (N + 127) // 128
@@ -317,8 +320,13 @@ def fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal: bool = False, scale: 
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if lse is None else lse
     _check_tensor("out", o, torch.bfloat16, (B, H, N, d))
     _check_tensor("lse", lse, torch.float32, (B, H, N))
-    st = lib.fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
-                        k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                        B, H, N, d, int(bool(causal)), _scale(scale, d), _stream())
-    _raise(st, "fa_fwd_fp8")
+    ptrs = (q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
+            k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(), lse.data_ptr())
+    if exp_mode == 0:
+        st = lib.fa_fwd_fp8(*ptrs, B, H, N, d, int(bool(causal)), _scale(scale, d), _stream())
+        _raise(st, "fa_fwd_fp8")
+    else:
+        st = lib.fa_fwd_fp8_ext(*ptrs, B, H, N, d, int(bool(causal)), _scale(scale, d),
+                                int(exp_mode), _stream())
+        _raise(st, "fa_fwd_fp8_ext")
     return o, lse

@@ -343,9 +343,15 @@ int fa_quant_fp8(const uint16_t* x, uint8_t* x8, float* scales, const int8_t* si
 int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
                const float* k_scale, const float* v_scale, uint16_t* o, float* lse,
                int B, int H, int N, int d, int causal, float scale, void* stream) {
-  if (!scalars_ok(causal, scale)) return FA_ERR_ARG;
+  return fa_fwd_fp8_ext(q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, causal, scale, 0, stream);
+}
+
+int fa_fwd_fp8_ext(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+                   const float* k_scale, const float* v_scale, uint16_t* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale, int exp_mode, void* stream) {
+  if (!scalars_ok(causal, scale) || exp_mode < 0 || exp_mode > 2) return FA_ERR_ARG;
   if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o || !lse) return FA_ERR_NULL;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if ((d != 64 && d != 128) || (exp_mode != 0 && d != 128)) return FA_ERR_HEADDIM;
   if (!shape_ok(B, H, N, d)) return FA_ERR_SHAPE;
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(q_scale) ||
       !aligned16(k_scale) || !aligned16(v_scale) || !aligned16(o) || !aligned16(lse))
@@ -356,7 +362,7 @@ int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const fl
   const Range outs[2] = {span(o, 2 * n), span(lse, (size_t)B * H * N * 4)};
   if (any_alias(outs, 2, ins, 6)) return FA_ERR_ALIAS;
   if (int st = check_device()) return st;
-  fa::Fp8FwdArgs a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, causal, scale, stream};
+  fa::Fp8FwdArgs a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, causal, scale, stream, exp_mode};
   return fa::launch_fwd_fp8(a) ? FA_ERR_LAUNCH : FA_OK;
 }
 

@@ -227,12 +227,35 @@ __device__ __forceinline__ void load_tile8_async(uint8_t* lds_tile, const uint8_
 
 }  // namespace
 
+// 2^x on the FMA units, the software exponential of [LIB] "FA4 — Blackwell's
+// asymmetry" (idea 1) and [LIN] "FA4 (2026)" (change 2), for x <= 8: x = n + f
+// with n = rint(x) (adding 1.5 * 2^23 leaves n in the low mantissa bits) and
+// f in [-1/2, 1/2]; 2^f by a degree-4 polynomial whose coefficients are a
+// weighted least-squares fit of 2^f on [-1/2, 1/2] (relative error at most
+// 2.7e-6 over x in [-126, 8]); 2^n added into the exponent field. Below -126
+// (masked scores are -inf) it returns 0, as v_exp_f32 does. Nine vector
+// instructions per value against one v_exp_f32, so it pays only where the
+// transcendental unit binds; here it does not (measured, see fa_fwd_fp8_ext).
+__device__ __forceinline__ float soft_exp2(float x) {
+  const float xc = fmaxf(x, -126.f);
+  const float t = xc + 12582912.f;
+  const float f = xc - (t - 12582912.f);
+  float p = __builtin_fmaf(0.009560510516166687f, f, 0.05591703951358795f);
+  p = __builtin_fmaf(p, f, 0.24024981260299683f);
+  p = __builtin_fmaf(p, f, 0.6931219696998596f);
+  p = __builtin_fmaf(p, f, 0.9999991655349731f);
+  const float r = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p) + (__builtin_bit_cast(uint32_t, t) << 23));
+  return x < -126.f ? 0.f : r;
+}
+
 // XCD (causal d = 128, chosen by the host when every round holds whole heads): the
 // grid holds one workgroup per resident slot, and XCD x (workgroup j runs on
 // XCD j % 8) takes heads x, x + 8, ..., all Q-blocks of a head per round,
 // the Q-block order reversed on odd rounds, as in the bf16 forward.
 // Otherwise one workgroup per (head, Q-block): the loop below runs once.
-template <int D, bool CAUSAL, int NW, bool XCD = false>
+// SEXP: which exponentials of the softmax run as soft_exp2 (0 none, 1 one
+// value in four, 2 all); d = 128 only.
+template <int D, bool CAUSAL, int NW, bool XCD = false, int SEXP = 0>
 __global__ void __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, const uint8_t* __restrict__ V8,
                const float* __restrict__ QS, const float* __restrict__ KSc, const float* __restrict__ VS,
@@ -372,7 +395,9 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
         float p[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          p[e] = fast_exp2(__builtin_fmaf(s[kb][4 * q4 + e], ct, off));
+          const float x = __builtin_fmaf(s[kb][4 * q4 + e], ct, off);
+          const bool sw = SEXP == 2 || (SEXP == 1 && e == 0);
+          p[e] = sw ? soft_exp2(x) : fast_exp2(x);
           rs += p[e];
         }
         // no clamp needed: m >= this tile's scaled maximum - kF8Lazy, so
@@ -456,9 +481,9 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8, c
   }  // items
 }
 
-// Workgroups of fwd_fp8_kernel<D, true, NW, true> resident on the current
-// device at once, looked up once per device.
-template <int D, int NW>
+// Workgroups of fwd_fp8_kernel<D, true, NW, true, SEXP> resident on the
+// current device at once, looked up once per device and instance.
+template <int D, int NW, int SEXP>
 static int f8_resident_slots() {
   constexpr int kMaxDev = 64;
   static std::atomic<int> cache[kMaxDev];
@@ -467,7 +492,7 @@ static int f8_resident_slots() {
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fwd_fp8_kernel<D, true, NW, true>, NW * 64, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fwd_fp8_kernel<D, true, NW, true, SEXP>, NW * 64, 0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
@@ -492,7 +517,7 @@ int launch_quant_fp8(const QuantArgs& a) {
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, int SEXP>
 static int launch_f8_nw(const Fp8FwdArgs& a) {
   constexpr int BR = NW * kF8QW;
   const int nqb = (a.N + BR - 1) / BR, nsb = (a.N + 127) / 128;
@@ -501,16 +526,16 @@ static int launch_f8_nw(const Fp8FwdArgs& a) {
   // Causal d = 128: persistent (2.7% faster at N = 8192, 15-18% at 1024 -
   // 2048). Not at d = 64, where the loop's registers cost a workgroup per CU.
   if constexpr (CAUSAL && D == 128) {
-    const int slots = f8_resident_slots<D, NW>();
+    const int slots = f8_resident_slots<D, NW, SEXP>();
     const int g = slots > 0 ? std::min(blocks, slots) : blocks;
     if (g % 8 == 0 && BH % 8 == 0 && (g / 8) % nqb == 0) {
-      hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, NW, true>), dim3((unsigned)g), dim3(NW * 64), 0,
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, NW, true, SEXP>), dim3((unsigned)g), dim3(NW * 64), 0,
                          (hipStream_t)a.stream, a.q8, a.k8, a.v8, a.qs, a.ks, a.vs, a.o, a.lse, BH, a.N, nqb,
                          nsb, a.scale * kLog2e);
       return hipGetLastError() == hipSuccess ? 0 : 1;
     }
   }
-  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+  hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL, NW, false, SEXP>), dim3((unsigned)blocks), dim3(NW * 64), 0,
                      (hipStream_t)a.stream, a.q8, a.k8, a.v8, a.qs, a.ks, a.vs, a.o, a.lse, BH, a.N, nqb,
                      nsb, a.scale * kLog2e);
   return hipGetLastError() == hipSuccess ? 0 : 1;
@@ -520,17 +545,26 @@ static int launch_f8_nw(const Fp8FwdArgs& a) {
 // at d = 64 (2-24%), and for non-causal d = 128 up to N = 2048; above that
 // the eight-wave workgroup was 2-4% faster.
 constexpr int kF8WideKeys = 2048;
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int SEXP>
 static int launch_f8(const Fp8FwdArgs& a) {
   if constexpr (D == 128 && !CAUSAL) {
-    if (a.N > kF8WideKeys) return launch_f8_nw<D, CAUSAL, 8>(a);
+    if (a.N > kF8WideKeys) return launch_f8_nw<D, CAUSAL, 8, SEXP>(a);
   }
-  return launch_f8_nw<D, CAUSAL, 4>(a);
+  return launch_f8_nw<D, CAUSAL, 4, SEXP>(a);
+}
+
+template <int SEXP>
+static int launch_f8_128(const Fp8FwdArgs& a) {
+  return a.causal ? launch_f8<128, true, SEXP>(a) : launch_f8<128, false, SEXP>(a);
 }
 
 int launch_fwd_fp8(const Fp8FwdArgs& a) {
-  if (a.d == 128) return a.causal ? launch_f8<128, true>(a) : launch_f8<128, false>(a);
-  return a.causal ? launch_f8<64, true>(a) : launch_f8<64, false>(a);
+  if (a.d == 128) {
+    if (a.exp_mode == 1) return launch_f8_128<1>(a);
+    if (a.exp_mode == 2) return launch_f8_128<2>(a);
+    return launch_f8_128<0>(a);
+  }
+  return a.causal ? launch_f8<64, true, 0>(a) : launch_f8<64, false, 0>(a);
 }
 
 }  // namespace fa

@@ -93,6 +93,7 @@ struct Fp8FwdArgs {
   int B, H, N, d, causal;
   float scale;
   void* stream;
+  int exp_mode = 0;  // exponentials of the softmax in software: 0 none, 1 one in four, 2 all (d = 128)
 };
 
 // Each returns 0 on a successful launch, nonzero if hipGetLastError reports one.

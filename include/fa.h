@@ -51,14 +51,14 @@ enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = 1,      /* a required pointer is NULL */
   FA_ERR_SHAPE = 2,     /* B, H or N < 1, the tensor is too large, or H_kv does not divide H */
-  FA_ERR_HEADDIM = 3,   /* d not 64, 128 or 256 (fp8: 64 or 128; rotation: 128) */
+  FA_ERR_HEADDIM = 3,   /* d not 64, 128 or 256 (fp8: 64 or 128; rotation and exp_mode 1, 2: 128) */
   FA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned, or a stride not a multiple of 8 */
   FA_ERR_WORKSPACE = 5, /* backward workspace NULL, misaligned or too small */
   FA_ERR_DEVICE = 6,    /* no HIP device, or the current device is not gfx950 */
   FA_ERR_ALIAS = 7,     /* an output overlaps an input, another output or itself */
   FA_ERR_LAUNCH = 8,    /* the kernel launch failed (hipGetLastError) */
   FA_ERR_ARG = 9,       /* causal not 0/1, a window side < -1 or > 2^24, scale not finite and positive,
-                           a stride < 1, or a row stride >= 2^31 */
+                           a stride < 1, a row stride >= 2^31, or exp_mode not 0, 1 or 2 */
   FA_ERR_SCRATCH = 10   /* fa_bwd_noalloc: 4 * B * H * N bytes exceed FA_BWD_NOALLOC_SCRATCH_BYTES */
 };
 
@@ -270,6 +270,24 @@ int fa_quant_fp8(const uint16_t* x, uint8_t* x8, float* scales, const int8_t* si
 int fa_fwd_fp8(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
                const float* k_scale, const float* v_scale, uint16_t* o, float* lse,
                int B, int H, int N, int d, int causal, float scale, void* stream);
+
+/*
+ * fa_fwd_fp8 with the softmax's exponentials chosen by exp_mode: the software
+ * 2^x of [LIB] "FA4 — Blackwell's asymmetry" (idea 1) and [LIN] "FA4 (2026)"
+ * (change 2), a polynomial on the FMA units (range reduction to n + f,
+ * 2^f by a degree-4 polynomial, 2^n into the exponent field; relative error
+ * at most 2.7e-6), in place of the transcendental instruction.
+ *   exp_mode : 0 the hardware exponential for every value (what fa_fwd_fp8
+ *              runs); 1 the software 2^x for one value in four; 2 for all.
+ *              Other values: FA_ERR_ARG. Modes 1 and 2 need d = 128
+ *              (else FA_ERR_HEADDIM).
+ * Other arguments, checks and outputs as fa_fwd_fp8. On this chip the
+ * software form costs more vector instructions than it saves, so mode 0 is
+ * the fast one; the others are for measuring that trade.
+ */
+int fa_fwd_fp8_ext(const uint8_t* q8, const uint8_t* k8, const uint8_t* v8, const float* q_scale,
+                   const float* k_scale, const float* v_scale, uint16_t* o, float* lse,
+                   int B, int H, int N, int d, int causal, float scale, int exp_mode, void* stream);
 
 #ifdef __cplusplus
 }

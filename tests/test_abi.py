@@ -116,6 +116,12 @@ def test_bwd_quant_fp8_reject_bad_arguments():
     f8 = [P + i * 0x100000 for i in range(8)]
     assert lib.fa_fwd_fp8(*f8[:7], None, 1, 1, 64, 64, 0, 0.125, None) == 1
     assert lib.fa_fwd_fp8(*f8, 1, 1, 64, 80, 0, 0.125, None) == 3
+    # software-exponential mode: 0, 1 or 2, and 1 or 2 only at d = 128
+    for mode in (-1, 3):
+        assert lib.fa_fwd_fp8_ext(*f8, 1, 1, 64, 128, 0, 0.125, mode, None) == 9
+    assert lib.fa_fwd_fp8_ext(*f8, 1, 1, 64, 64, 0, 0.125, 1, None) == 3
+    assert lib.fa_fwd_fp8_ext(*f8, 1, 1, 64, 64, 0, 0.125, 2, None) == 3
+    assert lib.fa_fwd_fp8_ext(*f8[:7], None, 1, 1, 64, 128, 0, 0.125, 1, None) == 1
 
 
 def _st(*triples):

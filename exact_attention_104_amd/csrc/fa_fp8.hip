@@ -36,37 +36,13 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
   return (uint32_t)r;
 }
 
-// Value of x held by lane (lane ^ M) of the same 16-lane row, M in {1, 2, 4, 8},
-// moved with DPP lane selects on the vector ALU (no LDS crossbar traffic):
-// quad_perm [1,0,3,2] and [2,3,0,1] for 1 and 2; for 4 the half-row mirror
-// (j -> j ^ 7 within 8 lanes) followed by quad_perm [3,2,1,0] (j -> j ^ 3);
-// for 8 a rotation of the row by 8 lanes.
-template <int M>
-__device__ __forceinline__ float row16_xor(float x) {
-  const int v = __builtin_bit_cast(int, x);
-  int r;
-  if constexpr (M == 1) r = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
-  else if constexpr (M == 2) r = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
-  else if constexpr (M == 4) r = __builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false), 0x1B, 0xF, 0xF, false);
-  else r = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
-  return __builtin_bit_cast(float, r);
-}
-
-// One butterfly stage across lanes c and c ^ M of a row: the lower lane keeps
-// the sum, the upper the difference (partner minus own value), both as
-// fma(x, +-1, partner): x * (+-1) is exact, so each is the one rounding of
-// x + partner or partner - x.
-template <int M>
-__device__ __forceinline__ void lane_butterfly(float (&x)[8], int c) {
-  const float sgn = (c & M) == 0 ? 1.f : -1.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = __builtin_fmaf(x[i], sgn, row16_xor<M>(x[i]));
-}
-
-template <int D, bool ROT>
+// Block quantiser without rotation: one workgroup per 128-row block, 8
+// values per lane, the block's amax reduced across the workgroup, then the
+// codes (fl32 amax / 448 the scale, x * fl32(448 / amax) clamped and rounded
+// to e4m3).
+template <int D>
 __global__ void __launch_bounds__(256)
-quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __restrict__ scales,
-             const int8_t* __restrict__ signs, int N, int nb) {
+quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __restrict__ scales, int N, int nb) {
   constexpr int LPR = D / 8;         // lanes per row, 8 values each
   constexpr int RPP = 256 / LPR;     // rows per pass
   constexpr int PASSES = 128 / RPP;  // passes over the 128-row block
@@ -77,13 +53,6 @@ quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __
   const int tid = threadIdx.x, c = tid % LPR, rr = tid / LPR;
   const size_t base = bh * (size_t)N * D;
 
-  // the random signs as sign-bit masks of the packed bf16 pairs (bits 15, 31)
-  uint32_t smask[4] = {0, 0, 0, 0};
-  if (ROT) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      smask[j] = (signs[c * 8 + 2 * j] < 0 ? 0x8000u : 0u) | (signs[c * 8 + 2 * j + 1] < 0 ? 0x80000000u : 0u);
-  }
   float x[PASSES][8];
   float amax = 0.f;
 #pragma unroll
@@ -91,40 +60,13 @@ quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __
     const int row = blk * 128 + p * RPP + rr;
     u32x4 u = {0, 0, 0, 0};
     if (row < N) u = *(const u32x4*)(X + base + (size_t)row * D + c * 8);
-    if (ROT) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) u[j] ^= smask[j];  // s o x: negation is a sign-bit flip
-    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       x[p][2 * j] = __builtin_bit_cast(float, u[j] << 16);
       x[p][2 * j + 1] = __builtin_bit_cast(float, u[j] & 0xffff0000u);
     }
-    if (ROT) {
-      // strides 1, 2, 4 inside the lane
 #pragma unroll
-      for (int h = 1; h < 8; h *= 2)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if ((i & h) == 0) {
-            const float a = x[p][i], b = x[p][i + h];
-            x[p][i] = a + b;
-            x[p][i + h] = a - b;
-          }
-      // strides 8, 16, 32, 64 across the row's 16 lanes
-      static_assert(!ROT || LPR == 16, "the rotation is defined for d = 128");
-      lane_butterfly<1>(x[p], c);
-      lane_butterfly<2>(x[p], c);
-      lane_butterfly<4>(x[p], c);
-      lane_butterfly<8>(x[p], c);
-      const float inv_sqrt128 = 0x1.6a09e6p-4f;  // fl32(1 / sqrt(128))
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[p][i] = x[p][i] * inv_sqrt128;
-    }
-    if (row < N) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[p][i]));
-    }
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[p][i]));  // rows past N hold zeros
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
@@ -143,6 +85,99 @@ quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __
       for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(x[p][i] * factor, -448.f), 448.f);
       const u32x2 out = {pack_e4m3x4(v[0], v[1], v[2], v[3]), pack_e4m3x4(v[4], v[5], v[6], v[7])};
       *(u32x2*)(X8 + base + (size_t)row * D + c * 8) = out;
+    }
+  }
+  if (tid == 0) scales[bh * nb + blk] = scale;
+}
+
+// Block quantiser with the random-sign Hadamard rotation (d = 128): x' =
+// H_128 (s o x) / sqrt(128) in fp32, as radix-2 butterflies (a, b) -> (a + b,
+// a - b) at strides 1, 2, 4, ..., 64 in that order, then the multiply by
+// fl32(1 / sqrt(128)). Two lanes per row: lane 2r + e holds columns 64 e ..
+// 64 e + 63 of row r of the block, so strides 1 .. 32 pair values inside the
+// lane and only stride 64 pairs the two lanes (one DPP exchange, lane ^ 1),
+// lane 0 keeping the sum and lane 1 the difference, its partner's value minus
+// its own, as fma(own, +-1, partner): own * (+-1) is exact, so each is the one
+// rounding of the sum or the difference (a - b itself, not b - a negated,
+// which would turn an exact zero into -0). So every value takes the same
+// roundings as in the stated order. The rotation is what
+// bounds this kernel (its loads and stores move as fast as the unrotated
+// one's): the layout leaves one cross-lane stage of seven, where 16 lanes of
+// 8 values per row needed four.
+__global__ void __launch_bounds__(256)
+quant_rot_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __restrict__ scales,
+                 const int8_t* __restrict__ signs, int N, int nb) {
+  constexpr int D = 128;
+  // the random signs as sign-bit masks of the packed bf16 pairs (bits 15, 31):
+  // negation is a sign-bit flip
+  __shared__ __attribute__((aligned(16))) uint32_t smask[D / 2];
+  __shared__ float wmax[4];
+
+  const int blk = (int)(blockIdx.x % nb);
+  const size_t bh = blockIdx.x / nb;
+  const int tid = threadIdx.x, e = tid & 1, row = blk * 128 + (tid >> 1);
+  const size_t base = bh * (size_t)N * D;
+  if (tid < D / 2)
+    smask[tid] = (signs[2 * tid] < 0 ? 0x8000u : 0u) | (signs[2 * tid + 1] < 0 ? 0x80000000u : 0u);
+
+  u32x4 u[8];
+  const uint16_t* src = X + base + (size_t)row * D + 64 * e;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) u[i] = u32x4{0, 0, 0, 0};
+  if (row < N) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = *(const u32x4*)(src + 8 * i);
+  }
+  __syncthreads();  // the masks are written
+  float x[64];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const u32x4 m = *(const u32x4*)(smask + 32 * e + 4 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = u[i][j] ^ m[j];
+      x[8 * i + 2 * j] = __builtin_bit_cast(float, w << 16);
+      x[8 * i + 2 * j + 1] = __builtin_bit_cast(float, w & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int h = 1; h < 64; h *= 2)
+#pragma unroll
+    for (int i = 0; i < 64; ++i)
+      if ((i & h) == 0) {
+        const float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+  // stride 64: lane 0 keeps own + partner, lane 1 partner - own
+  const float sgn = e ? -1.f : 1.f;
+  const float inv_sqrt128 = 0x1.6a09e6p-4f;  // fl32(1 / sqrt(128))
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const float p = __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x[i]), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+    x[i] = __builtin_fmaf(x[i], sgn, p) * inv_sqrt128;
+    amax = fmaxf(amax, fabsf(x[i]));  // rows past N hold zeros
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const bool zero = amax == 0.f;
+  const float scale = zero ? 1.f : __fdiv_rn(amax, 448.f);
+  const float factor = zero ? 1.f : __fdiv_rn(448.f, amax);
+  if (row < N) {
+    uint8_t* dst = X8 + base + (size_t)row * D + 64 * e;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v[16];
+#pragma unroll
+      for (int t = 0; t < 16; ++t) v[t] = fminf(fmaxf(x[16 * i + t] * factor, -448.f), 448.f);
+      const u32x4 out = {pack_e4m3x4(v[0], v[1], v[2], v[3]), pack_e4m3x4(v[4], v[5], v[6], v[7]),
+                         pack_e4m3x4(v[8], v[9], v[10], v[11]), pack_e4m3x4(v[12], v[13], v[14], v[15])};
+      *(u32x4*)(dst + 16 * i) = out;
     }
   }
   if (tid == 0) scales[bh * nb + blk] = scale;
@@ -508,11 +543,11 @@ int launch_quant_fp8(const QuantArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
   if (a.d == 128) {
     if (a.signs)
-      hipLaunchKernelGGL((quant_kernel<128, true>), grid, block, 0, st, a.x, a.x8, a.scales, a.signs, a.N, nb);
+      hipLaunchKernelGGL(quant_rot_kernel, grid, block, 0, st, a.x, a.x8, a.scales, a.signs, a.N, nb);
     else
-      hipLaunchKernelGGL((quant_kernel<128, false>), grid, block, 0, st, a.x, a.x8, a.scales, a.signs, a.N, nb);
+      hipLaunchKernelGGL((quant_kernel<128>), grid, block, 0, st, a.x, a.x8, a.scales, a.N, nb);
   } else {
-    hipLaunchKernelGGL((quant_kernel<64, false>), grid, block, 0, st, a.x, a.x8, a.scales, a.signs, a.N, nb);
+    hipLaunchKernelGGL((quant_kernel<64>), grid, block, 0, st, a.x, a.x8, a.scales, a.N, nb);
   }
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }

@@ -97,6 +97,27 @@ def test_quant_zero_block_and_rotation_needs_d128(gpu):
         gpu.quant_fp8(torch.zeros((1, 1, 8, 64), dtype=torch.bfloat16, device="cuda"), sd)
 
 
+def test_quant_rotation_exact_zero_differences(gpu):
+    """Rows whose sign-flipped halves are equal (x_{64+i} s_{64+i} = x_i s_i):
+    the butterflies up to stride 32 leave the two halves equal, so every
+    difference of the last stage (stride 64) is exactly zero and must come
+    out +0 (code 0x00), as the oracle's a - b gives, never -0 (0x80). The
+    kernel forms those differences on the second lane of each row; codes and
+    scales bit-exact against the oracle, on a ragged block."""
+    s, sd = _signs_dev()
+    rng = np.random.default_rng(64)
+    half = rng.standard_normal((1, 2, 150, 64)).astype(np.float32)
+    half = (half.view(np.uint32) & 0xFFFF0000).view(np.float32)  # bf16 values
+    flip = (s[:64].astype(np.float32) * s[64:].astype(np.float32))
+    x = np.concatenate([half, half * flip], axis=-1)
+    x8, sc = gpu.quant_fp8(torch.from_numpy(x).to(torch.bfloat16).cuda(), sd)
+    torch.cuda.synchronize()
+    codes, scales = F.quantize(x, s)
+    assert np.all(codes[..., 64:] == 0)
+    assert np.array_equal(x8.cpu().numpy(), codes)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), scales.view(np.uint32))
+
+
 def _fp8_case(gpu, B, H, N, d, causal, rot, seed):
     host, dev = inputs_on_device(B, H, N, d, seed, outliers=True)
     q = _quant_all(gpu, host, dev, rot)

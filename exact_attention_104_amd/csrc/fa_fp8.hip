@@ -93,46 +93,46 @@ quant_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __
 // Block quantiser with the random-sign Hadamard rotation (d = 128): x' =
 // H_128 (s o x) / sqrt(128) in fp32, as radix-2 butterflies (a, b) -> (a + b,
 // a - b) at strides 1, 2, 4, ..., 64 in that order, then the multiply by
-// fl32(1 / sqrt(128)). Two lanes per row: lane 2r + e holds columns 64 e ..
-// 64 e + 63 of row r of the block, so strides 1 .. 32 pair values inside the
-// lane and only stride 64 pairs the two lanes (one DPP exchange, lane ^ 1),
-// lane 0 keeping the sum and lane 1 the difference, its partner's value minus
-// its own, as fma(own, +-1, partner): own * (+-1) is exact, so each is the one
-// rounding of the sum or the difference (a - b itself, not b - a negated,
-// which would turn an exact zero into -0). So every value takes the same
-// roundings as in the stated order. The rotation is what
-// bounds this kernel (its loads and stores move as fast as the unrotated
-// one's): the layout leaves one cross-lane stage of seven, where 16 lanes of
-// 8 values per row needed four.
-__global__ void __launch_bounds__(256)
+// fl32(1 / sqrt(128)). Four lanes per row: lane 4r + e holds columns 32 e ..
+// 32 e + 31 of row r of the block, so strides 1 .. 16 pair values inside the
+// lane, and strides 32 and 64 pair lanes e ^ 1 and e ^ 2 of the same quad
+// (DPP quad permutations). In each cross-lane stage the lower lane keeps the
+// sum and the upper the difference, its partner's value minus its own, as
+// fma(own, +-1, partner): own * (+-1) is exact, so each is the one rounding of
+// the sum or the difference (a - b itself: b - a negated would turn an exact
+// zero into -0). So every value takes the same roundings as in the stated
+// order. 32 values per lane keep the kernel near 64 VGPRs, eight waves per
+// SIMD: its loads, butterflies and stores then overlap across more
+// workgroups than with 64 values per lane.
+__global__ void __launch_bounds__(512)
 quant_rot_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __restrict__ scales,
                  const int8_t* __restrict__ signs, int N, int nb) {
   constexpr int D = 128;
   // the random signs as sign-bit masks of the packed bf16 pairs (bits 15, 31):
   // negation is a sign-bit flip
   __shared__ __attribute__((aligned(16))) uint32_t smask[D / 2];
-  __shared__ float wmax[4];
+  __shared__ float wmax[8];
 
   const int blk = (int)(blockIdx.x % nb);
   const size_t bh = blockIdx.x / nb;
-  const int tid = threadIdx.x, e = tid & 1, row = blk * 128 + (tid >> 1);
+  const int tid = threadIdx.x, e = tid & 3, row = blk * 128 + (tid >> 2);
   const size_t base = bh * (size_t)N * D;
   if (tid < D / 2)
     smask[tid] = (signs[2 * tid] < 0 ? 0x8000u : 0u) | (signs[2 * tid + 1] < 0 ? 0x80000000u : 0u);
 
-  u32x4 u[8];
-  const uint16_t* src = X + base + (size_t)row * D + 64 * e;
+  u32x4 u[4];
+  const uint16_t* src = X + base + (size_t)row * D + 32 * e;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) u[i] = u32x4{0, 0, 0, 0};
+  for (int i = 0; i < 4; ++i) u[i] = u32x4{0, 0, 0, 0};
   if (row < N) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) u[i] = *(const u32x4*)(src + 8 * i);
+    for (int i = 0; i < 4; ++i) u[i] = *(const u32x4*)(src + 8 * i);
   }
   __syncthreads();  // the masks are written
-  float x[64];
+  float x[32];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const u32x4 m = *(const u32x4*)(smask + 32 * e + 4 * i);
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 m = *(const u32x4*)(smask + 16 * e + 4 * i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t w = u[i][j] ^ m[j];
@@ -141,37 +141,45 @@ quant_rot_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float
     }
   }
 #pragma unroll
-  for (int h = 1; h < 64; h *= 2)
+  for (int h = 1; h < 32; h *= 2)
 #pragma unroll
-    for (int i = 0; i < 64; ++i)
+    for (int i = 0; i < 32; ++i)
       if ((i & h) == 0) {
         const float a = x[i], b = x[i + h];
         x[i] = a + b;
         x[i + h] = a - b;
       }
-  // stride 64: lane 0 keeps own + partner, lane 1 partner - own
-  const float sgn = e ? -1.f : 1.f;
+  // stride 32: lanes e, e ^ 1 (quad_perm [1,0,3,2]); stride 64: lanes e, e ^ 2
+  // (quad_perm [2,3,0,1])
+  const float s32 = (e & 1) ? -1.f : 1.f, s64 = (e & 2) ? -1.f : 1.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float p = __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x[i]), 0xB1, 0xF, 0xF, false));
+    x[i] = __builtin_fmaf(x[i], s32, p);
+  }
   const float inv_sqrt128 = 0x1.6a09e6p-4f;  // fl32(1 / sqrt(128))
   float amax = 0.f;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
+  for (int i = 0; i < 32; ++i) {
     const float p = __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x[i]), 0xB1, 0xF, 0xF, false));  // lane ^ 1
-    x[i] = __builtin_fmaf(x[i], sgn, p) * inv_sqrt128;
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x[i]), 0x4E, 0xF, 0xF, false));
+    x[i] = __builtin_fmaf(x[i], s64, p) * inv_sqrt128;
     amax = fmaxf(amax, fabsf(x[i]));  // rows past N hold zeros
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   if ((tid & 63) == 0) wmax[tid >> 6] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  amax = fmaxf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])),
+               fmaxf(fmaxf(wmax[4], wmax[5]), fmaxf(wmax[6], wmax[7])));
   const bool zero = amax == 0.f;
   const float scale = zero ? 1.f : __fdiv_rn(amax, 448.f);
   const float factor = zero ? 1.f : __fdiv_rn(448.f, amax);
   if (row < N) {
-    uint8_t* dst = X8 + base + (size_t)row * D + 64 * e;
+    uint8_t* dst = X8 + base + (size_t)row * D + 32 * e;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
       float v[16];
 #pragma unroll
       for (int t = 0; t < 16; ++t) v[t] = fminf(fmaxf(x[16 * i + t] * factor, -448.f), 448.f);
@@ -543,7 +551,7 @@ int launch_quant_fp8(const QuantArgs& a) {
   hipStream_t st = (hipStream_t)a.stream;
   if (a.d == 128) {
     if (a.signs)
-      hipLaunchKernelGGL(quant_rot_kernel, grid, block, 0, st, a.x, a.x8, a.scales, a.signs, a.N, nb);
+      hipLaunchKernelGGL(quant_rot_kernel, grid, dim3(512), 0, st, a.x, a.x8, a.scales, a.signs, a.N, nb);
     else
       hipLaunchKernelGGL((quant_kernel<128>), grid, block, 0, st, a.x, a.x8, a.scales, a.N, nb);
   } else {

@@ -102,8 +102,9 @@ def test_quant_rotation_exact_zero_differences(gpu):
     the butterflies up to stride 32 leave the two halves equal, so every
     difference of the last stage (stride 64) is exactly zero and must come
     out +0 (code 0x00), as the oracle's a - b gives, never -0 (0x80). The
-    kernel forms those differences on the second lane of each row; codes and
-    scales bit-exact against the oracle, on a ragged block."""
+    kernel forms those differences on the lanes that hold columns 64 to 127
+    (the upper pair of each row's four lanes); codes and scales bit-exact
+    against the oracle, on a ragged block."""
     s, sd = _signs_dev()
     rng = np.random.default_rng(64)
     half = rng.standard_normal((1, 2, 150, 64)).astype(np.float32)

@@ -96,8 +96,9 @@ def test_bwd_outputs_covered_unseen_key_blocks(gpu):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
-def test_fwd_fp8_outputs_covered(gpu, d, causal):
+@pytest.mark.parametrize("d,exp_mode", [(64, 0), (128, 0), (128, 1), (128, 2)])
+def test_fwd_fp8_outputs_covered(gpu, d, exp_mode, causal):
+    """exp_mode 1 and 2 (the software 2^x) are separate kernel instances."""
     B, H, N = 2, 3, 777
     host = fa_inputs.attention_inputs(B, H, N, d, 7500 + d, outliers=True)
     dev = {n: to_dev(host[n]) for n in host}
@@ -105,10 +106,10 @@ def test_fwd_fp8_outputs_covered(gpu, d, causal):
     go = Guarded((B, H, N, d), torch.bfloat16)
     gl = Guarded((B, H, N), torch.float32)
     gpu.fwd_fp8(qz["q"][0], qz["k"][0], qz["v"][0], qz["q"][1], qz["k"][1], qz["v"][1], causal=causal,
-                out=go.t, lse=gl.t)
+                out=go.t, lse=gl.t, exp_mode=exp_mode)
     torch.cuda.synchronize()
-    go.check("fp8 O d%d c%d" % (d, causal))
-    gl.check("fp8 LSE d%d c%d" % (d, causal))
+    go.check("fp8 O d%d c%d mode %d" % (d, causal, exp_mode))
+    gl.check("fp8 LSE d%d c%d mode %d" % (d, causal, exp_mode))
     deq = {n: F.dequantize(qz[n][0].cpu().numpy(), qz[n][1].cpu().numpy()) for n in ("q", "k", "v")}
     r_o, _ = A.forward(deq["q"], deq["k"], deq["v"], causal, 1.0 / math.sqrt(d))
     e = A.rel_rms(to_host(go.t), r_o)
@@ -180,11 +181,13 @@ def test_bwd_dq_persistent_dealing_covers_outputs(gpu):
         assert e <= GRAD_REL_RMS, h
 
 
-def test_fwd_fp8_persistent_dealing_covers_outputs(gpu):
+@pytest.mark.parametrize("exp_mode", [0, 2])
+def test_fwd_fp8_persistent_dealing_covers_outputs(gpu, exp_mode):
     """Causal d = 128 fp8 forward on its persistent grid (each XCD taking all
     Q-blocks of a head per round, four rounds, the order reversed on odd
-    rounds): O and LSE written once and nothing outside them; two heads
-    against the fp64 oracle on the dequantised inputs."""
+    rounds), with the hardware and the software exponential: O and LSE
+    written once and nothing outside them; two heads against the fp64 oracle
+    on the dequantised inputs."""
     B, H, N, d = 16, 16, 1024, 128
     host = fa_inputs.attention_inputs(B, H, N, d, 7600, outliers=True)
     dev = {n: to_dev(host[n]) for n in host}
@@ -192,10 +195,10 @@ def test_fwd_fp8_persistent_dealing_covers_outputs(gpu):
     go = Guarded((B, H, N, d), torch.bfloat16)
     gl = Guarded((B, H, N), torch.float32)
     gpu.fwd_fp8(qz["q"][0], qz["k"][0], qz["v"][0], qz["q"][1], qz["k"][1], qz["v"][1], causal=True,
-                out=go.t, lse=gl.t)
+                out=go.t, lse=gl.t, exp_mode=exp_mode)
     torch.cuda.synchronize()
-    go.check("fp8 persistent O")
-    gl.check("fp8 persistent LSE")
+    go.check("fp8 persistent O mode %d" % exp_mode)
+    gl.check("fp8 persistent LSE mode %d" % exp_mode)
     o_h = to_host(go.t)
     for b, h in ((0, 0), (B - 1, H - 1)):
         deq = {n: F.dequantize(qz[n][0][b:b + 1, h:h + 1].cpu().numpy(), qz[n][1][b:b + 1, h:h + 1].cpu().numpy())

@@ -275,8 +275,10 @@ __device__ __forceinline__ void load_tile8_async(uint8_t* lds_tile, const uint8_
 // with n = rint(x) (adding 1.5 * 2^23 leaves n in the low mantissa bits) and
 // f in [-1/2, 1/2]; 2^f by a degree-4 polynomial whose coefficients are a
 // weighted least-squares fit of 2^f on [-1/2, 1/2] (relative error at most
-// 2.7e-6 over x in [-126, 8]); 2^n added into the exponent field. Below -126
-// (masked scores are -inf) it returns 0, as v_exp_f32 does. Nine vector
+// 2.7e-6 over x in [-125.5, 8]); 2^n added into the exponent field. Between
+// -126 and -125.5 that sum leaves the normal range (values below 2^-125,
+// nothing next to a row's largest p, which is at least 1); below -126
+// (masked scores are -inf) it returns 0. Nine vector
 // instructions per value against one v_exp_f32, so it pays only where the
 // transcendental unit binds; here it does not (measured, see fa_fwd_fp8_ext).
 __device__ __forceinline__ float soft_exp2(float x) {

@@ -228,8 +228,8 @@ def _fp8_modes(gpu, q, causal, modes):
 
 
 @pytest.mark.parametrize("mode", [1, 2])
-@pytest.mark.parametrize("N,causal,rot", [(300, False, False), (300, True, True), (700, True, False),
-                                          (2049, False, True)])
+@pytest.mark.parametrize("N,causal,rot", [(1, True, True), (65, False, False), (300, False, False),
+                                          (300, True, True), (700, True, False), (2049, False, True)])
 def test_fwd_fp8_software_exp(gpu, N, causal, rot, mode):
     """exp_mode 1 and 2 at d = 128: reading (i) against the oracle at the bar
     of mode 0 (rel-RMS of O, every LSE within the MFMA accumulation bound),

@@ -42,6 +42,24 @@ def test_bwd_noalloc_matches_fa_bwd_twice(gpu):
         assert e <= GRAD_REL_RMS
 
 
+def test_bwd_noalloc_at_the_scratch_limit(gpu):
+    """B * H * N = 2^21 rows: D fills the 8 MiB scratch exactly (the largest
+    problem the entry point accepts), so the last rows of D sit at its very
+    end. The gradients equal fa_bwd's bit for bit."""
+    B, H, N, d = 64, 32, 1024, 64
+    assert 4 * B * H * N == 8 << 20
+    g = torch.Generator(device="cuda")
+    g.manual_seed(8300)
+    q, k, v, do = (torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(4))
+    o, lse = gpu.fwd(q, k, v, causal=True)
+    ref = gpu.bwd(q, k, v, o, do, lse, causal=True)
+    outs = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+    got = gpu.bwd_noalloc(q, k, v, o, do, lse, causal=True, out=outs)
+    torch.cuda.synchronize()
+    for name, a_, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert torch.equal(a_, r), "noalloc at the limit: %s differs from fa_bwd" % name
+
+
 def test_bwd_noalloc_rejects_too_large(gpu):
     """B * H * N rows of D beyond the 8 MiB scratch: FA_ERR_SCRATCH, nothing launched."""
     B, H, N, d = 1, 33, 65536, 64  # 2162688 rows > 2^21

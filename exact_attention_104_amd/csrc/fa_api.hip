@@ -330,7 +330,8 @@ int fa_quant_fp8(const uint16_t* x, uint8_t* x8, float* scales, const int8_t* si
   if (!x || !x8 || !scales) return FA_ERR_NULL;
   if ((d != 64 && d != 128) || (signs_or_null && d != 128)) return FA_ERR_HEADDIM;
   if (!shape_ok(B, H, N, d)) return FA_ERR_SHAPE;
-  if (!aligned16(x) || !aligned16(x8) || !aligned16(scales)) return FA_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(x8) || !aligned16(scales) || (signs_or_null && !aligned16(signs_or_null)))
+    return FA_ERR_ALIGN;
   const size_t n = (size_t)B * H * N * d, nb = (size_t)B * H * ((N + 127) / 128) * 4;
   const Range ins[2] = {span(x, 2 * n), span(signs_or_null, signs_or_null ? 128 : 0)};
   const Range outs[2] = {span(x8, n), span(scales, nb)};

@@ -108,18 +108,12 @@ __global__ void __launch_bounds__(512)
 quant_rot_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float* __restrict__ scales,
                  const int8_t* __restrict__ signs, int N, int nb) {
   constexpr int D = 128;
-  // the random signs as sign-bit masks of the packed bf16 pairs (bits 15, 31):
-  // negation is a sign-bit flip
-  __shared__ __attribute__((aligned(16))) uint32_t smask[D / 2];
   __shared__ float wmax[8];
 
   const int blk = (int)(blockIdx.x % nb);
   const size_t bh = blockIdx.x / nb;
   const int tid = threadIdx.x, e = tid & 3, row = blk * 128 + (tid >> 2);
   const size_t base = bh * (size_t)N * D;
-  if (tid < D / 2)
-    smask[tid] = (signs[2 * tid] < 0 ? 0x8000u : 0u) | (signs[2 * tid + 1] < 0 ? 0x80000000u : 0u);
-
   u32x4 u[4];
   const uint16_t* src = X + base + (size_t)row * D + 32 * e;
 #pragma unroll
@@ -128,14 +122,21 @@ quant_rot_kernel(const uint16_t* __restrict__ X, uint8_t* __restrict__ X8, float
 #pragma unroll
     for (int i = 0; i < 4; ++i) u[i] = *(const u32x4*)(src + 8 * i);
   }
-  __syncthreads();  // the masks are written
+  // the random signs of this lane's 32 columns, loaded after the values (one
+  // wait covers both) and by every lane: a table in LDS behind a barrier
+  // held each workgroup back by the latency of one wave's load
+  const u32x4 sg[2] = {*(const u32x4*)(signs + 32 * e), *(const u32x4*)(signs + 32 * e + 16)};
   float x[32];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x4 m = *(const u32x4*)(smask + 16 * e + 4 * i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t w = u[i][j] ^ m[j];
+      // negation is a sign-bit flip: the sign bits (bit 7) of the pair's two
+      // int8 signs, moved to bits 15 and 31 of the packed bf16 pair
+      const uint32_t sw = sg[i >> 1][2 * (i & 1) + (j >> 1)];
+      const uint32_t m = (j & 1) ? (((sw >> 8) & 0x8000u) | (sw & 0x80000000u))
+                                 : (((sw << 8) & 0x8000u) | ((sw << 16) & 0x80000000u));
+      const uint32_t w = u[i][j] ^ m;
       x[8 * i + 2 * j] = __builtin_bit_cast(float, w << 16);
       x[8 * i + 2 * j + 1] = __builtin_bit_cast(float, w & 0xffff0000u);
     }

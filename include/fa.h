@@ -249,7 +249,8 @@ int fa_bwd_ext(const uint16_t* q, const uint16_t* k, const uint16_t* v, const ui
  *   scales        : out, fp32 [B, H, ceil(N / 128)]; scale = fl32(amax / 448),
  *                   1 for an all-zero block
  *   signs_or_null : in, device int8 [128] of +-1 (rotation x' = H_128 (s o x) /
- *                   sqrt(128), d must be 128), or NULL for no rotation
+ *                   sqrt(128), d must be 128; 16-byte aligned like every
+ *                   tensor here, else FA_ERR_ALIGN), or NULL for no rotation
  * Codes: e4m3_rne_saturating(fl32(x' * fl32(448 / amax))). Rotation order:
  * multiply by s, butterflies (a, b) -> (a + b, a - b) at strides 1, 2, ..., 64,
  * multiply by fl32(1 / sqrt(128)), all in fp32.

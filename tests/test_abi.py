@@ -113,6 +113,8 @@ def test_bwd_quant_fp8_reject_bad_arguments():
     assert lib.fa_quant_fp8(P, None, P + 0x200000, None, 1, 1, 64, 64, None) == 1
     assert lib.fa_quant_fp8(P, P + 0x100000 + 4, P + 0x200000, None, 1, 1, 64, 64, None) == 4
     assert lib.fa_quant_fp8(P, P + 0x40, P + 0x200000, None, 1, 1, 64, 64, None) == 7
+    # the rotation's signs are 16-byte aligned like every tensor
+    assert lib.fa_quant_fp8(P, P + 0x100000, P + 0x200000, P + 0x300000 + 8, 1, 1, 64, 128, None) == 4
     f8 = [P + i * 0x100000 for i in range(8)]
     assert lib.fa_fwd_fp8(*f8[:7], None, 1, 1, 64, 64, 0, 0.125, None) == 1
     assert lib.fa_fwd_fp8(*f8, 1, 1, 64, 80, 0, 0.125, None) == 3
